@@ -1,0 +1,188 @@
+"""Benchmark of the MXFP4 hot path on one MI355X (gfx950).
+
+One step = row-wise BF16 -> MXFP4 quantize of the activation A [M, K] plus the
+block-scaled GEMM C = dq(A) dq(B)^T against pre-quantized weights B [N, K],
+on the square workload M = N = K = 8192 with BF16 output (the headline MXFP4
+GEMM shape). Inputs are seeded synthetic BF16 (N(0,1) with 1% of entries x100)
+resident in HBM before the timed region.
+
+Prints one JSON line:
+  value        2*M*N*K / (time per step), TFLOP/s, whole step (quantize + GEMM)
+  roofline     the GEMM kernel against the FP4 MFMA dense peak (10.1 PFLOP/s):
+               achieved = 2*M*N*K / mean GEMM launch time, measured with HIP
+               events recorded on the launch stream around every timed launch
+  cpu_baseline the float64 NumPy oracle on a bounded sample of the same
+               workload (a 2048 x 2048 block of C over the full K, including
+               the oracle's quantize of the 4096 operand rows it needs)
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+FP4_DENSE_PEAK_TFLOPS = 10100.0   # MI355X dense MXFP4 MFMA peak
+HBM_PEAK_GBPS = 8000.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="square")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "gemm_traffic.json"),
+                   help="HBM bytes per GEMM launch from rocprofv3 counters, if measured")
+    return p.parse_args()
+
+
+def cpu_baseline(a_bits, b_bits, K, rows=2048, cols=2048):
+    import oracle
+    cores = len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    ac, as_ = oracle.quantize(a_bits[:rows])
+    bc, bs = oracle.quantize(b_bits[:cols])
+    c, _s = oracle.gemm_block(ac, as_, bc, bs)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * rows * cols * K
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": (f"C block {rows}x{cols} over K={K}: oracle quantize of {rows}+{cols} rows, "
+                   f"float64 dequantize, C and S matmuls; {dt:.2f} s wall"),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the path needs no collective; see the sharding notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import block_scaled_microscaling_amd as mx
+    from synth import WORKLOADS, bf16_matrix
+
+    w = WORKLOADS[args.workload]
+    M, N, K = w.M, w.N, w.K
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if mx.mxfp4_available() != 1:
+        raise RuntimeError("libmxfp4: no gfx950 device")
+
+    print(f"bench: workload {w.name} M={M} N={N} K={K}; generating inputs", file=sys.stderr,
+          flush=True)
+    a_bits = bf16_matrix((M, K), w.a_dist, w.a_seed)
+    b_bits = bf16_matrix((N, K), w.b_dist, w.b_seed)
+    x = torch.from_numpy(a_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    wts = torch.from_numpy(b_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    out_dtype = torch.float32 if w.out_dtype == mx.OUT_FP32 else torch.bfloat16
+
+    # Pre-quantized weights and preallocated buffers: nothing is allocated
+    # inside the timed region.
+    bc, bs = mx.quantize(wts)
+    ac = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+    as_ = torch.empty((M, K // 32), dtype=torch.uint8, device=dev)
+    c = torch.empty((M, N), dtype=out_dtype, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        mx.quantize(x, ac, as_)
+        if ev is not None:
+            ev[1].record(stream)
+        mx.gemm(ac, as_, bc, bs, out=c)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    stop.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+
+    ms_total = start.elapsed_time(stop)
+    ms_step = ms_total / args.steps
+    q_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    g_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    flops = 2.0 * M * N * K
+    gemm_tflops = flops / (g_ms.mean() * 1e-3) / 1e12
+    q_bytes = M * K * 2 + M * K // 2 + M * K // 32
+    quant_gbps = q_bytes / (q_ms.mean() * 1e-3) / 1e9
+
+    traffic = None
+    if os.path.exists(args.traffic_json):
+        try:
+            with open(args.traffic_json) as f:
+                t = json.load(f)
+            if t.get("workload") == w.name:
+                traffic = t.get("bytes_per_launch")
+        except (OSError, ValueError):
+            traffic = None
+
+    result = {
+        "metric": "MXFP4 GEMM TFLOP/s (2MNK) at 8192^3 + % of FP4 MFMA peak; quantize GB/s",
+        "value": flops / (ms_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp4",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"{w.name}: quantize A[{M},{K}] BF16 -> MXFP4, then GEMM "
+                         f"{M}x{N}x{K} against pre-quantized B[{N},{K}], "
+                         f"{'fp32' if w.out_dtype else 'bf16'} out"),
+            "M": M, "N": N, "K": K,
+            "out_dtype": "fp32" if w.out_dtype else "bf16",
+        },
+        "gemm_tflops": gemm_tflops,
+        "gemm_ms": float(g_ms.mean()),
+        "quantize_gbps": quant_gbps,
+        "quantize_ms": float(q_ms.mean()),
+        "quantize_hbm_frac": quant_gbps / HBM_PEAK_GBPS,
+        "wall_s_timed": t_wall,
+        "roofline": {
+            "bound": "mfma",
+            "achieved": gemm_tflops,
+            "peak": FP4_DENSE_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": gemm_tflops / FP4_DENSE_PEAK_TFLOPS,
+            "traffic": traffic,
+        },
+    }
+    if not args.no_cpu_baseline:
+        print("bench: timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(a_bits, b_bits, K)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,156 @@
+"""MXFP4 quantize and block-scaled GEMM on AMD gfx950 (MI355X).
+
+A thin binding over the C ABI of libmxfp4.so (include/mxfp4.h). Every step
+of the computation runs in the library's HIP kernels; this module only
+marshals arguments. PyTorch supplies device memory and streams.
+
+Two layers, same names as the C ABI:
+  * mxfp4_available, mxfp4_strerror, mxfp4_quantize, mxfp4_quantize_async,
+    mxfp4_gemm take raw device pointers (ints) and return the C status code.
+  * quantize(x) and gemm(...) take torch tensors, check their dtype, device,
+    shape and contiguity, allocate outputs when none are given, enqueue on
+    torch's current stream and raise Mxfp4Error on a non-zero status.
+
+If the library is missing the functions raise: there is no fallback path.
+"""
+
+import ctypes
+import os
+
+__all__ = [
+    "Mxfp4Error", "OUT_BF16", "OUT_FP32", "library_path", "load_library",
+    "mxfp4_available", "mxfp4_strerror", "mxfp4_quantize", "mxfp4_quantize_async",
+    "mxfp4_gemm", "quantize", "gemm",
+]
+
+OUT_BF16 = 0
+OUT_FP32 = 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libmxfp4.so")
+_lib = None
+
+
+class Mxfp4Error(RuntimeError):
+    def __init__(self, rc, what):
+        super().__init__(f"{what} failed: rc={rc} ({mxfp4_strerror(rc)})")
+        self.rc = rc
+
+
+def load_library():
+    """Load libmxfp4.so once; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(library_path):
+            raise RuntimeError(
+                f"{library_path} is missing: build it with "
+                "`python -m block_scaled_microscaling_amd.build`")
+        lib = ctypes.CDLL(library_path)
+        vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        lib.mxfp4_available.argtypes = []
+        lib.mxfp4_available.restype = i32
+        lib.mxfp4_strerror.argtypes = [i32]
+        lib.mxfp4_strerror.restype = ctypes.c_char_p
+        lib.mxfp4_quantize.argtypes = [vp, i64, i64, vp, vp]
+        lib.mxfp4_quantize.restype = i32
+        lib.mxfp4_quantize_async.argtypes = [vp, i64, i64, vp, vp, vp]
+        lib.mxfp4_quantize_async.restype = i32
+        lib.mxfp4_gemm.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, vp, vp]
+        lib.mxfp4_gemm.restype = i32
+        _lib = lib
+    return _lib
+
+
+# ----------------------------------------------------------- raw C ABI names
+def mxfp4_available():
+    return int(load_library().mxfp4_available())
+
+
+def mxfp4_strerror(rc):
+    return load_library().mxfp4_strerror(int(rc)).decode()
+
+
+def mxfp4_quantize(x_bf16, M, K, codes_out, scales_out):
+    return int(load_library().mxfp4_quantize(x_bf16, M, K, codes_out, scales_out))
+
+
+def mxfp4_quantize_async(x_bf16, M, K, codes_out, scales_out, stream):
+    return int(load_library().mxfp4_quantize_async(x_bf16, M, K, codes_out, scales_out, stream))
+
+
+def mxfp4_gemm(A_codes, A_scales, B_codes, B_scales, M, N, K, out_dtype, C, stream):
+    return int(load_library().mxfp4_gemm(A_codes, A_scales, B_codes, B_scales, M, N, K,
+                                         out_dtype, C, stream))
+
+
+# ------------------------------------------------------- torch tensor layer
+def _stream_handle(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _check(t, name, dtype, shape):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (row-major)")
+
+
+def quantize(x, codes=None, scales=None, stream=None):
+    """Row-wise BF16 -> MXFP4. x: bfloat16 [M, K] on the GPU.
+
+    Returns (codes uint8 [M, K/2], scales uint8 [M, K/32]).
+    """
+    import torch
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [M, K]")
+    M, K = x.shape
+    _check(x, "x", torch.bfloat16, (M, K))
+    if codes is None:
+        codes = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((M, K // 32), dtype=torch.uint8, device=x.device)
+    _check(codes, "codes", torch.uint8, (M, K // 2))
+    _check(scales, "scales", torch.uint8, (M, K // 32))
+    rc = mxfp4_quantize_async(x.data_ptr(), M, K, codes.data_ptr(), scales.data_ptr(),
+                              _stream_handle(stream))
+    if rc != 0:
+        raise Mxfp4Error(rc, "mxfp4_quantize")
+    return codes, scales
+
+
+def gemm(A_codes, A_scales, B_codes, B_scales, out_dtype=None, out=None, stream=None):
+    """C[M, N] = dq(A) @ dq(B)^T from packed MXFP4 operands (B is N x K).
+
+    out_dtype: torch.bfloat16 (default) or torch.float32.
+    """
+    import torch
+    if out_dtype is None:
+        out_dtype = out.dtype if out is not None else torch.bfloat16
+    if out_dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("out_dtype must be torch.bfloat16 or torch.float32")
+    if A_codes.dim() != 2 or B_codes.dim() != 2:
+        raise ValueError("code tensors must be 2-D")
+    M, K = A_codes.shape[0], A_codes.shape[1] * 2
+    N = B_codes.shape[0]
+    _check(A_codes, "A_codes", torch.uint8, (M, K // 2))
+    _check(B_codes, "B_codes", torch.uint8, (N, K // 2))
+    _check(A_scales, "A_scales", torch.uint8, (M, K // 32))
+    _check(B_scales, "B_scales", torch.uint8, (N, K // 32))
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=A_codes.device)
+    _check(out, "out", out_dtype, (M, N))
+    code = OUT_FP32 if out_dtype == torch.float32 else OUT_BF16
+    rc = mxfp4_gemm(A_codes.data_ptr(), A_scales.data_ptr(), B_codes.data_ptr(),
+                    B_scales.data_ptr(), M, N, K, code, out.data_ptr(), _stream_handle(stream))
+    if rc != 0:
+        raise Mxfp4Error(rc, "mxfp4_gemm")
+    return out

@@ -1,0 +1,115 @@
+// C ABI of libmxfp4.so (declared in include/mxfp4.h).
+//
+// Every entry point validates all of its arguments before enqueuing
+// anything, checks once per device that the device is gfx950, and maps HIP
+// launch errors to MXFP4_ELAUNCH. The return-code scheme (0 = ok, distinct
+// negative codes, an availability probe) follows the review of the stub
+// library on "Initial integration of a4w4 GEMM" (ROCm/TransformerEngine
+// #663); the per-call checks are the capability gates of the hipBLASLt MXFP4
+// path on "Integrate MXFP4 hipblaslt GEMM support" (#697, Changes list); the
+// arch check that never falls back to a default follows "feat(ck-tile):
+// aquant GEMM TE to dispatcher bridge" (rocm-libraries #9980, summary).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "../../include/mxfp4.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+constexpr int64_t kMaxDim = 2147483647;      // 2^31 - 1
+constexpr int64_t kMaxBytes = int64_t(1) << 40;
+
+// Per-device state: 0 = not checked yet, 1 = gfx950 and ready, -1 = not usable.
+std::atomic<int> g_device_state[kMaxDevices];
+
+int check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return MXFP4_EUNSUPPORTED;
+  }
+  int state = g_device_state[dev].load(std::memory_order_acquire);
+  if (state == 0) {
+    hipDeviceProp_t prop;
+    state = -1;
+    if (hipGetDeviceProperties(&prop, dev) == hipSuccess &&
+        strncmp(prop.gcnArchName, "gfx950", 6) == 0 &&
+        (prop.gcnArchName[6] == '\0' || prop.gcnArchName[6] == ':') &&
+        mxfp4::init_kernels_for_current_device() == hipSuccess)
+      state = 1;
+    (void)hipGetLastError();
+    g_device_state[dev].store(state, std::memory_order_release);
+  }
+  return state == 1 ? MXFP4_OK : MXFP4_EUNSUPPORTED;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int launch_status(hipError_t e) { return e == hipSuccess ? MXFP4_OK : MXFP4_ELAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+int mxfp4_available(void) { return check_device() == MXFP4_OK ? 1 : 0; }
+
+const char* mxfp4_strerror(int rc) {
+  switch (rc) {
+    case MXFP4_OK:
+      return "success";
+    case MXFP4_EINVAL:
+      return "invalid argument (size, null pointer or out_dtype)";
+    case MXFP4_EUNSUPPORTED:
+      return "no usable gfx950 device is current";
+    case MXFP4_ELAUNCH:
+      return "HIP kernel launch failed";
+    case MXFP4_EALIGN:
+      return "pointer not aligned as required";
+    default:
+      return "unknown mxfp4 status";
+  }
+}
+
+int mxfp4_quantize_async(const void* x_bf16, int64_t M, int64_t K, void* codes_out,
+                         void* scales_out, void* stream) {
+  if (!x_bf16 || !codes_out || !scales_out) return MXFP4_EINVAL;
+  if (M < 1 || K < 32 || K % 32 != 0 || M > kMaxDim || K > kMaxDim) return MXFP4_EINVAL;
+  if (M * K >= kMaxBytes) return MXFP4_EINVAL;
+  if (!aligned(x_bf16, 16) || !aligned(codes_out, 4)) return MXFP4_EALIGN;
+  const int dev = check_device();
+  if (dev != MXFP4_OK) return dev;
+  return launch_status(mxfp4::launch_quantize(x_bf16, M * (K / 32), codes_out, scales_out,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+int mxfp4_quantize(const void* x_bf16, int64_t M, int64_t K, void* codes_out, void* scales_out) {
+  return mxfp4_quantize_async(x_bf16, M, K, codes_out, scales_out, nullptr);
+}
+
+int mxfp4_gemm(const void* A_codes, const void* A_scales, const void* B_codes,
+               const void* B_scales, int64_t M, int64_t N, int64_t K, int out_dtype, void* C,
+               void* stream) {
+  if (!A_codes || !A_scales || !B_codes || !B_scales || !C) return MXFP4_EINVAL;
+  if (M <= 0 || N <= 0 || K <= 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim)
+    return MXFP4_EINVAL;
+  if (K % 256 != 0 || M % 32 != 0 || N % 32 != 0) return MXFP4_EINVAL;
+  if (out_dtype != MXFP4_OUT_BF16 && out_dtype != MXFP4_OUT_FP32) return MXFP4_EINVAL;
+  const int64_t out_bytes = out_dtype == MXFP4_OUT_FP32 ? 4 : 2;
+  if (M * (K / 2) >= kMaxBytes || N * (K / 2) >= kMaxBytes || M * N * out_bytes >= kMaxBytes)
+    return MXFP4_EINVAL;
+  if (!aligned(A_codes, 16) || !aligned(B_codes, 16) || !aligned(A_scales, 4) ||
+      !aligned(B_scales, 4) || !aligned(C, 16))
+    return MXFP4_EALIGN;
+  const int dev = check_device();
+  if (dev != MXFP4_OK) return dev;
+  return launch_status(mxfp4::launch_gemm(A_codes, A_scales, B_codes, B_scales, (int)M, (int)N,
+                                          (int)K, out_dtype == MXFP4_OUT_FP32, C,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,22 @@
+// Host-side launchers of the gfx950 kernels, called by the C ABI in api.hip.
+// Arguments are validated by the caller; the launchers only size the grid,
+// enqueue on `stream` and report hipGetLastError().
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mxfp4 {
+
+// Row-wise BF16 -> MXFP4 over the flat [M*K/32] block sequence.
+hipError_t launch_quantize(const void* x_bf16, int64_t nblocks, void* codes, void* scales,
+                           hipStream_t stream);
+
+// C[M,N] = A[M,K] * B[N,K]^T with block scales; out_fp32 selects FP32 vs BF16.
+hipError_t launch_gemm(const void* A, const void* As, const void* B, const void* Bs, int M,
+                       int N, int K, bool out_fp32, void* C, hipStream_t stream);
+
+// One-time per-device set-up of kernel attributes (large LDS allocations).
+hipError_t init_kernels_for_current_device();
+
+}  // namespace mxfp4

@@ -1,0 +1,89 @@
+/*
+ * mxfp4.h -- C ABI of libmxfp4.so: row-wise BF16 -> MXFP4 quantize and the
+ * block-scaled MXFP4 x MXFP4 ("a4w4") GEMM on AMD Instinct gfx950 (MI355X).
+ *
+ * Format ("Integrate MXFP4 hipblaslt GEMM support", ROCm/TransformerEngine
+ * #697, Changes list): an MXFP4 operand is FP4 E2M1 elements with one UE8M0
+ * power-of-two scale per 32 consecutive K elements. Layouts used here:
+ *   codes   uint8 [rows, K/2]  row-major; element 2i in bits 3:0, 2i+1 in 7:4
+ *   scales  uint8 [rows, K/32] row-major; value 2^(byte - 127)
+ *   E2M1    bit 3 sign, magnitudes {0, 0.5, 1, 1.5, 2, 3, 4, 6}
+ *
+ * Ownership and threading, for every entry point below:
+ *   - All data pointers are DEVICE pointers owned by the caller. The library
+ *     never allocates, frees, copies or synchronizes; work is enqueued
+ *     asynchronously on `stream` (a hipStream_t; NULL = the default stream).
+ *   - Every argument is validated before anything is enqueued. A non-zero
+ *     return means nothing was enqueued and no output was written.
+ *   - The arch check runs once per device; calls are thread-safe.
+ *
+ * Return codes follow the stub convention reviewed on "Initial integration
+ * of a4w4 GEMM" (ROCm/TransformerEngine #663): 0 on success, a distinct
+ * negative code per failure class, plus an availability probe.
+ */
+#ifndef MXFP4_H
+#define MXFP4_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum mxfp4_out_dtype { MXFP4_OUT_BF16 = 0, MXFP4_OUT_FP32 = 1 };
+
+enum mxfp4_status {
+  MXFP4_OK = 0,
+  MXFP4_EINVAL = -1,       /* a size, pointer or out_dtype is invalid        */
+  MXFP4_EUNSUPPORTED = -2, /* current device is not gfx950, or no device    */
+  MXFP4_ELAUNCH = -3,      /* the HIP runtime reported an error at launch   */
+  MXFP4_EALIGN = -4        /* a pointer lacks the alignment stated below    */
+};
+
+/* 1 if the current HIP device is gfx950 and the kernels are loadable, else
+ * 0. Never fails; suggested on the a4w4 integration page as the probe a
+ * framework checks before routing to this backend. */
+int mxfp4_available(void);
+
+/* Static, human-readable text for a return code (never NULL). */
+const char* mxfp4_strerror(int rc);
+
+/* Row-wise BF16 -> MXFP4 quantize, one 32-element block at a time: the
+ * quantizer role of MXFP4Quantizer on "Integrate MXFP4 hipblaslt GEMM
+ * support" (plain, un-shuffled data and scales). For each block:
+ *   amax  = max |x| over its 32 BF16 values
+ *   e     = clamp(floor(log2 amax) - 2, -127, 127)   (e = -127 if amax == 0)
+ *   scale = e + 127
+ *   code  = sign(x) | E2M1 magnitude nearest to |x| / 2^e, ties to the even
+ *           code, saturating at 6; the sign bit is kept on zero results.
+ * x_bf16     [M, K] BF16, row-major, 16-byte aligned
+ * codes_out  [M, K/2] uint8, 4-byte aligned
+ * scales_out [M, K/32] uint8
+ * Requires M >= 1, K >= 32, K % 32 == 0, M * K < 2^40, finite inputs
+ * (NaN/Inf in a block give unspecified bytes for that block only).
+ * mxfp4_quantize enqueues on the default stream; _async on `stream`. */
+int mxfp4_quantize(const void* x_bf16, int64_t M, int64_t K, void* codes_out,
+                   void* scales_out);
+int mxfp4_quantize_async(const void* x_bf16, int64_t M, int64_t K, void* codes_out,
+                         void* scales_out, void* stream);
+
+/* Block-scaled GEMM, TN: C[m, n] = sum_k dq(A[m, k]) * dq(B[n, k]) with
+ * dq(code, scale) = E2M1(code) * 2^(scale - 127), fp32 accumulation; the
+ * capability gates of the hipBLASLt MXFP4 path on "Integrate MXFP4 hipblaslt
+ * GEMM support" (Changes list) are this function's contract:
+ *   K % 256 == 0, M % 32 == 0, N % 32 == 0, M, N, K > 0,
+ *   out_dtype MXFP4_OUT_BF16 (round to nearest even) or MXFP4_OUT_FP32,
+ *   no bias, alpha = 1, beta = 0 (C is overwritten, never read).
+ * A_codes [M, K/2], B_codes [N, K/2]: 16-byte aligned
+ * A_scales [M, K/32], B_scales [N, K/32]: 4-byte aligned
+ * C [M, N] row-major BF16 or FP32: 16-byte aligned
+ * M, N, K <= 2^31 - 1 and each buffer < 2^40 bytes. */
+int mxfp4_gemm(const void* A_codes, const void* A_scales, const void* B_codes,
+               const void* B_scales, int64_t M, int64_t N, int64_t K, int out_dtype,
+               void* C, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXFP4_H */

@@ -1,0 +1,111 @@
+"""Host-side checks of the C ABI in libmxfp4.so (no GPU work is launched).
+
+Return codes follow the stub/probe convention reviewed on "Initial
+integration of a4w4 GEMM" (ROCm/TransformerEngine #663); the argument gates
+are those of the hipBLASLt MXFP4 path on "Integrate MXFP4 hipblaslt GEMM
+support" (#697, Changes list). Every call here fails validation, or finds no
+gfx950 device, before anything is enqueued.
+"""
+
+import os
+import re
+
+import pytest
+
+import block_scaled_microscaling_amd as mx
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                      "include", "mxfp4.h")
+
+OK, EINVAL, EUNSUPPORTED, ELAUNCH, EALIGN = 0, -1, -2, -3, -4
+P16 = 1 << 20           # stand-in pointer values: never dereferenced here
+P_ODD = (1 << 20) + 2
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mxfp4_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = mx.load_library()
+    names = _declared_functions()
+    assert names == ["mxfp4_available", "mxfp4_gemm", "mxfp4_quantize",
+                     "mxfp4_quantize_async", "mxfp4_strerror"]
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_strerror_texts():
+    for rc in (OK, EINVAL, EUNSUPPORTED, ELAUNCH, EALIGN):
+        assert mx.mxfp4_strerror(rc) and "unknown" not in mx.mxfp4_strerror(rc)
+    assert "unknown" in mx.mxfp4_strerror(12345)
+
+
+@pytest.mark.parametrize("M,N,K", [
+    (0, 32, 256), (32, 0, 256), (32, 32, 0), (-32, 32, 256),
+    (33, 32, 256), (32, 48, 256), (32, 32, 128), (32, 32, 384),
+    (1 << 31, 32, 256), (32, 32, (1 << 31) + 256),
+])
+def test_gemm_rejects_bad_sizes(M, N, K):
+    assert mx.mxfp4_gemm(P16, P16, P16, P16, M, N, K, mx.OUT_BF16, P16, None) == EINVAL
+
+
+def test_gemm_rejects_bad_dtype_and_nulls():
+    assert mx.mxfp4_gemm(P16, P16, P16, P16, 32, 32, 256, 2, P16, None) == EINVAL
+    assert mx.mxfp4_gemm(P16, P16, P16, P16, 32, 32, 256, -1, P16, None) == EINVAL
+    for i in range(5):
+        ptrs = [P16] * 5
+        ptrs[i] = None
+        a, as_, b, bs, c = ptrs
+        assert mx.mxfp4_gemm(a, as_, b, bs, 32, 32, 256, mx.OUT_FP32, c, None) == EINVAL
+
+
+def test_gemm_rejects_oversized_buffers():
+    # M * N * 4 bytes >= 2^40
+    assert mx.mxfp4_gemm(P16, P16, P16, P16, 1 << 20, 1 << 18, 256, mx.OUT_FP32, P16,
+                         None) == EINVAL
+
+
+def test_gemm_rejects_misaligned():
+    args = dict(A=P16, As=P16, B=P16, Bs=P16, C=P16)
+    for key, bad in [("A", P_ODD), ("B", P_ODD), ("C", P16 + 8), ("As", P16 + 2),
+                     ("Bs", P16 + 1)]:
+        a = dict(args)
+        a[key] = bad
+        rc = mx.mxfp4_gemm(a["A"], a["As"], a["B"], a["Bs"], 32, 32, 256, mx.OUT_BF16,
+                           a["C"], None)
+        assert rc == EALIGN, key
+
+
+@pytest.mark.parametrize("M,K", [(0, 32), (-1, 32), (4, 0), (4, 16), (4, 48), (4, 33),
+                                 (1 << 31, 32), (1 << 20, 1 << 20)])
+def test_quantize_rejects_bad_sizes(M, K):
+    assert mx.mxfp4_quantize(P16, M, K, P16, P16) == EINVAL
+    assert mx.mxfp4_quantize_async(P16, M, K, P16, P16, None) == EINVAL
+
+
+def test_quantize_rejects_nulls_and_misalignment():
+    assert mx.mxfp4_quantize(None, 4, 32, P16, P16) == EINVAL
+    assert mx.mxfp4_quantize(P16, 4, 32, None, P16) == EINVAL
+    assert mx.mxfp4_quantize(P16, 4, 32, P16, None) == EINVAL
+    assert mx.mxfp4_quantize(P16 + 8, 4, 32, P16, P16) == EALIGN
+    assert mx.mxfp4_quantize(P16, 4, 32, P16 + 2, P16) == EALIGN
+
+
+def test_no_device_reports_unsupported():
+    """Valid arguments with no gfx950 device current: rc -2, nothing launched."""
+    if mx.mxfp4_available() != 0:
+        pytest.skip("a gfx950 device is present; stand-in pointers must not reach it")
+    assert mx.mxfp4_gemm(P16, P16, P16, P16, 32, 32, 256, mx.OUT_BF16, P16, None) == EUNSUPPORTED
+    assert mx.mxfp4_quantize(P16, 4, 32, P16, P16) == EUNSUPPORTED
+
+
+def test_tensor_layer_validates_before_calling():
+    import torch
+    x = torch.zeros((4, 64), dtype=torch.float32)
+    with pytest.raises(TypeError):
+        mx.quantize(x)
+    with pytest.raises(ValueError):
+        mx.quantize(torch.zeros(4, dtype=torch.bfloat16))

@@ -1,0 +1,202 @@
+"""GPU parity of the MXFP4 GEMM against the CPU oracle.
+
+Operation: the FP4 x FP4 ("a4w4") GEMM of "Initial integration of a4w4 GEMM"
+(ROCm/TransformerEngine #663) under the gates of the hipBLASLt MXFP4 path on
+"Integrate MXFP4 hipblaslt GEMM support" (#697, Changes list). FP32 output
+must be within 1e-5 * sum|a*b| of the float64 oracle; BF16 output within one
+BF16 step of the oracle rounded to BF16 (with the near-cancellation reading
+documented in oracle/compare.py). The non-zero count check guards against the
+silent all-zeros failure reported on "feat(ck-tile): aquant GEMM TE to
+dispatcher bridge" (rocm-libraries #9980, GPU validation).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_microscaling_amd as mx
+import oracle
+from conftest import read_golden
+from gpu_helpers import (DEV, announce, bf16_bits_of_tensor, bf16_to_dev, check_gemm_output,
+                         sample_pairs, u8_to_dev)
+from synth import WORKLOADS, bf16_matrix, random_codes, random_scales
+
+pytestmark = pytest.mark.gpu
+
+
+def _assert_not_silent_zeros(got, c_ref, s_ref):
+    """Every output the oracle puts clearly away from zero is non-zero."""
+    significant = np.abs(c_ref) > 2 * oracle.FP32_REL_TOL * s_ref
+    assert significant.sum() > 0
+    assert np.count_nonzero(got[significant]) == int(significant.sum())
+
+
+def _gemm(Ac, As, Bc, Bs, out_dtype):
+    out = mx.gemm(u8_to_dev(Ac), u8_to_dev(As), u8_to_dev(Bc), u8_to_dev(Bs), out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_single_tile_random(out_dtype):
+    """One 32 x 32 x 256 problem: pins the MFMA operand/scale lane layout."""
+    announce(f"gemm 32x32x256 random {out_dtype}")
+    Ac, Bc = random_codes(32, 256, 1), random_codes(32, 256, 2)
+    As, Bs = random_scales(32, 256, 3), random_scales(32, 256, 4)
+    out = _gemm(Ac, As, Bc, Bs, out_dtype)
+    c_ref, s_ref = oracle.gemm(Ac, As, Bc, Bs)
+    check_gemm_output(out, c_ref, s_ref)
+
+
+def test_hand_worked_g1_padded():
+    """Q1 block x unit B rows (1 x 32 x 32 by hand), padded to 32 x 32 x 256
+    with zero codes: row 0 of C is the dequantized Q1 block."""
+    announce("gemm G1 padded")
+    g = read_golden("q1_block.txt")
+    Ac = np.zeros((32, 128), np.uint8)
+    Ac[0, :16] = [int(v, 16) for v in g["packed"]]
+    As = np.full((32, 8), 127, np.uint8)
+    Bc = np.zeros((32, 128), np.uint8)
+    for n in range(32):
+        Bc[n, n // 2] = 2 << (4 * (n % 2))
+    out = _gemm(Ac, As, Bc, As, torch.float32).cpu().numpy()
+    assert out[0].tolist() == [float(v) for v in g["dequant"]]
+    assert np.all(out[1:] == 0)
+
+
+def test_hand_worked_g2_g3_g4():
+    announce("gemm G2 G3 G4")
+    n = np.arange(32)
+    m = np.arange(32)[:, None]
+    # G2: C = 255 * 2^(n % 3)
+    A = np.full((32, 128), 0x22, np.uint8)
+    As = np.tile(np.arange(123, 131, dtype=np.uint8), (32, 1))
+    Bs = (126 + n % 3).astype(np.uint8)[:, None].repeat(8, axis=1)
+    for dt in (torch.float32, torch.bfloat16):
+        out = _gemm(A, As, A, Bs, dt).float().cpu().numpy()
+        assert np.array_equal(out, np.tile(255.0 * 2.0 ** (n % 3), (32, 1)))
+    # G3: nibble pairing, C = 448 everywhere
+    s = np.full((32, 8), 127, np.uint8)
+    out = _gemm(np.full((32, 128), 0x13, np.uint8), s, np.full((32, 128), 0x24, np.uint8), s,
+                torch.float32).cpu().numpy()
+    assert np.all(out == 448.0)
+    # G4: scale-to-block mapping, C = 2338 * 2^(m%2 + n%4 - 2)
+    A = np.zeros((32, 128), np.uint8)
+    for j in range(8):
+        A[:, 16 * j:16 * (j + 1)] = j | (j << 4)
+    As = (123 + np.arange(8)[None, :] + (np.arange(32) % 2)[:, None]).astype(np.uint8)
+    B = np.full((32, 128), 0x22, np.uint8)
+    Bs = (125 + n % 4).astype(np.uint8)[:, None].repeat(8, axis=1)
+    out = _gemm(A, As, B, Bs, torch.float32).cpu().numpy()
+    assert np.array_equal(out, 2338.0 * 2.0 ** ((m % 2) + (n[None, :] % 4) - 2))
+
+
+@pytest.mark.parametrize("M,N,K", [(32, 32, 256), (256, 256, 256), (288, 544, 512),
+                                   (544, 288, 1024), (64, 800, 768), (512, 96, 2304),
+                                   (800, 1056, 256)])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_random_operands_many_tiles(M, N, K, out_dtype):
+    """Uniform random code bytes (every code, both signs) and scales 117..137,
+    shapes spanning several 256-tiles with ragged M and N edges."""
+    announce(f"gemm random {M}x{N}x{K} {out_dtype}")
+    Ac, Bc = random_codes(M, K, M + 1), random_codes(N, K, N + 2)
+    As, Bs = random_scales(M, K, K + 3), random_scales(N, K, K + 4)
+    out = _gemm(Ac, As, Bc, Bs, out_dtype)
+    c_ref, s_ref = oracle.gemm(Ac, As, Bc, Bs)
+    check_gemm_output(out, c_ref, s_ref)
+    _assert_not_silent_zeros(out.float().cpu().numpy(), c_ref, s_ref)
+
+
+def test_wide_scale_range():
+    """Scales 100..150 on both sides: products span 2^-54 .. 2^46."""
+    announce("gemm wide scale range")
+    M, N, K = 96, 160, 1280
+    Ac, Bc = random_codes(M, K, 31), random_codes(N, K, 32)
+    As, Bs = random_scales(M, K, 33, 100, 150), random_scales(N, K, 34, 100, 150)
+    out = _gemm(Ac, As, Bc, Bs, torch.float32)
+    c_ref, s_ref = oracle.gemm(Ac, As, Bc, Bs)
+    check_gemm_output(out, c_ref, s_ref)
+
+
+def test_scale_doubling_is_exact():
+    """Adding 1 to every A scale of one row doubles that C row bit for bit
+    (power-of-two scaling commutes with fp32 rounding) and leaves the others."""
+    announce("gemm scale doubling invariant")
+    M, N, K = 64, 288, 1024
+    Ac, Bc = random_codes(M, K, 41), random_codes(N, K, 42)
+    As, Bs = random_scales(M, K, 43), random_scales(N, K, 44)
+    c0 = _gemm(Ac, As, Bc, Bs, torch.float32).cpu().numpy()
+    As2 = As.copy()
+    As2[17] += 1
+    c1 = _gemm(Ac, As2, Bc, Bs, torch.float32).cpu().numpy()
+    assert np.array_equal(c1[17], 2 * c0[17])
+    assert np.array_equal(np.delete(c1, 17, axis=0), np.delete(c0, 17, axis=0))
+
+
+def test_output_written_exactly_in_bounds():
+    announce("gemm canary")
+    M, N, K = 288, 320, 512
+    Ac, Bc = random_codes(M, K, 51), random_codes(N, K, 52)
+    As, Bs = random_scales(M, K, 53), random_scales(N, K, 54)
+    pad = 4096
+    buf = torch.full((M * N + 2 * pad,), 12345.0, dtype=torch.float32, device=DEV)
+    out = buf[pad:pad + M * N].view(M, N)
+    mx.gemm(u8_to_dev(Ac), u8_to_dev(As), u8_to_dev(Bc), u8_to_dev(Bs), out=out)
+    torch.cuda.synchronize()
+    b = buf.cpu().numpy()
+    assert np.all(b[:pad] == 12345.0) and np.all(b[-pad:] == 12345.0)
+    c_ref, s_ref = oracle.gemm(Ac, As, Bc, Bs)
+    check_gemm_output(out, c_ref, s_ref)
+
+
+def test_side_stream():
+    announce("gemm on a side stream")
+    M, N, K = 256, 512, 768
+    Ac, Bc = random_codes(M, K, 61), random_codes(N, K, 62)
+    As, Bs = random_scales(M, K, 63), random_scales(N, K, 64)
+    args = [u8_to_dev(t) for t in (Ac, As, Bc, Bs)]
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        out = mx.gemm(*args, out_dtype=torch.bfloat16)
+    s.synchronize()
+    c_ref, s_ref = oracle.gemm(Ac, As, Bc, Bs)
+    check_gemm_output(out, c_ref, s_ref)
+
+
+@pytest.mark.parametrize("name", ["tiny", "skinny", "square", "mlp_gate_up", "mlp_down", "ragged"])
+def test_workload_full_size(name):
+    """The workload end to end at full size: GPU quantize of A and B, GPU GEMM;
+    the oracle quantizes the sampled rows itself and computes the sampled
+    outputs (random pairs plus the bottom-right corner, which holds the
+    ragged tile edges)."""
+    w = WORKLOADS[name]
+    announce(f"workload {name}: {w.M}x{w.N}x{w.K} out={'fp32' if w.out_dtype else 'bf16'}")
+    a_bits = bf16_matrix((w.M, w.K), w.a_dist, w.a_seed)
+    b_bits = bf16_matrix((w.N, w.K), w.b_dist, w.b_seed)
+    ac, as_ = mx.quantize(bf16_to_dev(a_bits))
+    bc, bs = mx.quantize(bf16_to_dev(b_bits))
+    out_dtype = torch.float32 if w.out_dtype == mx.OUT_FP32 else torch.bfloat16
+    out = mx.gemm(ac, as_, bc, bs, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+
+    m_idx, n_idx = sample_pairs(w.M, w.N, 3000, seed=len(name))
+    rows_a = np.unique(m_idx)
+    rows_b = np.unique(n_idx)
+    ra_c, ra_s = oracle.quantize(a_bits[rows_a])
+    rb_c, rb_s = oracle.quantize(b_bits[rows_b])
+    # GPU codes of the sampled rows are the oracle's, bit for bit.
+    ridx_a = torch.from_numpy(rows_a).to(DEV)
+    ridx_b = torch.from_numpy(rows_b).to(DEV)
+    assert np.array_equal(ac[ridx_a].cpu().numpy(), ra_c)
+    assert np.array_equal(as_[ridx_a].cpu().numpy(), ra_s)
+    assert np.array_equal(bc[ridx_b].cpu().numpy(), rb_c)
+    assert np.array_equal(bs[ridx_b].cpu().numpy(), rb_s)
+    # Oracle outputs at the sampled pairs, from the oracle's own codes.
+    pos_a = np.searchsorted(rows_a, m_idx)
+    pos_b = np.searchsorted(rows_b, n_idx)
+    c_ref, s_ref = oracle.gemm_entries(ra_c, ra_s, rb_c, rb_s, pos_a, pos_b)
+    got = out[torch.from_numpy(m_idx).to(DEV), torch.from_numpy(n_idx).to(DEV)]
+    misses = check_gemm_output(got, c_ref, s_ref)
+    print(f"[gpu] {name}: {m_idx.size} sampled outputs, literal BF16 misses {misses}", flush=True)
+    _assert_not_silent_zeros(got.float().cpu().numpy(), c_ref, s_ref)
