@@ -53,12 +53,19 @@ __device__ __forceinline__ uint32_t quad_max(uint32_t v) {
   return max(v, o);  // quad_perm [2,3,0,1]
 }
 
+// The word is passed by value: a bit cast applied straight to a vector
+// element (q.y) was seen to read element 0 instead.
+__device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(bf16x2_t, w);
+}
+
 __device__ __forceinline__ uint32_t encode8(u32x4_t q, float scale) {
+  const uint32_t w0 = q[0], w1 = q[1], w2 = q[2], w3 = q[3];
   uint32_t r = 0;
-  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(bf16x2_t, q.x), scale, 0);
-  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(bf16x2_t, q.y), scale, 1);
-  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(bf16x2_t, q.z), scale, 2);
-  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(bf16x2_t, q.w), scale, 3);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, as_bf16x2(w0), scale, 0);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, as_bf16x2(w1), scale, 1);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, as_bf16x2(w2), scale, 2);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, as_bf16x2(w3), scale, 3);
   return r;
 }
 

@@ -110,7 +110,7 @@ def test_workload_inputs_sampled_rows(name):
 
 def test_misaligned_input_rejected():
     announce("quantize misaligned pointer")
-    base = torch.zeros(4 * 64 + 8, dtype=torch.bfloat16, device=DEV)
+    base = torch.zeros(4 * 64 + 4, dtype=torch.bfloat16, device=DEV)
     x = base[4:].view(4, 64)                                    # 8-byte offset
     codes = torch.empty((4, 32), dtype=torch.uint8, device=DEV)
     scales = torch.empty((4, 2), dtype=torch.uint8, device=DEV)
