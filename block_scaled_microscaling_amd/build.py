@@ -22,7 +22,7 @@ def hipcc_command(out=LIB):
     return [
         hipcc, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-        "-Wno-unused-command-line-argument",
+        "-Wno-unused-command-line-argument", "-Wno-inline-asm",
         "-o", out,
     ] + [os.path.join(CSRC, s) for s in SOURCES]
 
