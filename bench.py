@@ -12,8 +12,8 @@ Prints one JSON line:
                achieved = 2*M*N*K / mean GEMM launch time, measured with HIP
                events recorded on the launch stream around every timed launch
   cpu_baseline the float64 NumPy oracle on a bounded sample of the same
-               workload (a 2048 x 2048 block of C over the full K, including
-               the oracle's quantize of the 4096 operand rows it needs)
+               workload (a 4096 x 8192 block of C over the full K, including
+               the oracle's quantize of the 12288 operand rows it needs)
 """
 
 import argparse
@@ -41,10 +41,47 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "gemm_traffic.json"),
                    help="HBM bytes per GEMM launch from rocprofv3 counters, if measured")
+    p.add_argument("--copy-calibration-mib", type=int, default=0,
+                   help="only run a plain device copy of this many MiB three times and exit "
+                        "(the known-size kernel that scales the FETCH_SIZE/WRITE_SIZE counters)")
     return p.parse_args()
 
 
-def cpu_baseline(a_bits, b_bits, K, rows=2048, cols=2048):
+def gemm_source_digest():
+    """SHA-256 of the GEMM kernel source: counters taken on another source are stale."""
+    import hashlib
+    path = os.path.join(ROOT, "block_scaled_microscaling_amd", "csrc", "gemm.hip")
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def read_traffic(path, workload):
+    """HBM bytes per GEMM launch measured by rocprofv3 for this workload, or None."""
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("workload") != workload or t.get("gemm_source_sha256") != gemm_source_digest():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def copy_calibration(mib):
+    import torch
+    dev = torch.device("cuda:0")
+    n = mib << 20
+    src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}), flush=True)
+
+
+def cpu_baseline(a_bits, b_bits, K, rows=4096, cols=8192):
     import oracle
     cores = len(os.sched_getaffinity(0))
     t0 = time.perf_counter()
@@ -69,6 +106,9 @@ def main():
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the path needs no collective; see the sharding notes)", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration_mib:
+        copy_calibration(args.copy_calibration_mib)
+        return
 
     import torch
 
@@ -133,15 +173,7 @@ def main():
     q_bytes = M * K * 2 + M * K // 2 + M * K // 32
     quant_gbps = q_bytes / (q_ms.mean() * 1e-3) / 1e9
 
-    traffic = None
-    if os.path.exists(args.traffic_json):
-        try:
-            with open(args.traffic_json) as f:
-                t = json.load(f)
-            if t.get("workload") == w.name:
-                traffic = t.get("bytes_per_launch")
-        except (OSError, ValueError):
-            traffic = None
+    traffic = read_traffic(args.traffic_json, w.name)
 
     result = {
         "metric": "MXFP4 GEMM TFLOP/s (2MNK) at 8192^3 + % of FP4 MFMA peak; quantize GB/s",

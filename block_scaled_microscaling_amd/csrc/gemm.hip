@@ -377,7 +377,7 @@ void gemm_tile_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int wy = wave >> 2;  // 128-row half of the A tile
   const int wx = wave & 3;   // 64-row quarter of the B tile
   const int r = lane & 31;
