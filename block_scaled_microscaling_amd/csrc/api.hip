@@ -23,6 +23,7 @@ namespace {
 constexpr int kMaxDevices = 64;
 constexpr int64_t kMaxDim = 2147483647;      // 2^31 - 1
 constexpr int64_t kMaxBytes = int64_t(1) << 40;
+constexpr int64_t kMaxGemmK = int64_t(1) << 24;  // per-lane row offsets of the GEMM kernels are 32-bit
 
 // Per-device state: 0 = not checked yet, 1 = gfx950 and ready, -1 = not usable.
 std::atomic<int> g_device_state[kMaxDevices];
@@ -97,7 +98,7 @@ int mxfp4_gemm(const void* A_codes, const void* A_scales, const void* B_codes,
   if (!A_codes || !A_scales || !B_codes || !B_scales || !C) return MXFP4_EINVAL;
   if (M <= 0 || N <= 0 || K <= 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim)
     return MXFP4_EINVAL;
-  if (K % 256 != 0 || M % 32 != 0 || N % 32 != 0) return MXFP4_EINVAL;
+  if (K % 256 != 0 || M % 32 != 0 || N % 32 != 0 || K > kMaxGemmK) return MXFP4_EINVAL;
   if (out_dtype != MXFP4_OUT_BF16 && out_dtype != MXFP4_OUT_FP32) return MXFP4_EINVAL;
   const int64_t out_bytes = out_dtype == MXFP4_OUT_FP32 ? 4 : 2;
   if (M * (K / 2) >= kMaxBytes || N * (K / 2) >= kMaxBytes || M * N * out_bytes >= kMaxBytes)
@@ -107,9 +108,13 @@ int mxfp4_gemm(const void* A_codes, const void* A_scales, const void* B_codes,
     return MXFP4_EALIGN;
   const int dev = check_device();
   if (dev != MXFP4_OK) return dev;
+  const bool fp32 = out_dtype == MXFP4_OUT_FP32;
+  const auto st = static_cast<hipStream_t>(stream);
+  if (M <= mxfp4::kSkinnyMaxM)
+    return launch_status(mxfp4::launch_gemm_skinny(A_codes, A_scales, B_codes, B_scales, (int)M,
+                                                   (int)N, (int)K, fp32, C, st));
   return launch_status(mxfp4::launch_gemm(A_codes, A_scales, B_codes, B_scales, (int)M, (int)N,
-                                          (int)K, out_dtype == MXFP4_OUT_FP32, C,
-                                          static_cast<hipStream_t>(stream)));
+                                          (int)K, fp32, C, st));
 }
 
 }  // extern "C"

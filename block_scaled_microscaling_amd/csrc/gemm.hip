@@ -55,13 +55,11 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "gfx950.h"
 #include "kernels.h"
 
 namespace mxfp4 {
 namespace {
-
-typedef int v8i_t __attribute__((ext_vector_type(8)));
-typedef float v16f_t __attribute__((ext_vector_type(16)));
 
 constexpr int kThreads = 512;
 constexpr int kTileM = 256;
@@ -83,27 +81,6 @@ struct __align__(16) Slot {
   uint8_t a[kTileBytes];
   uint8_t b[kTileBytes];
 };
-
-// XOR swizzle of the 16-byte chunk index within a 128-byte LDS row.
-__device__ __forceinline__ int chunk_swizzle(int row) {
-  return (row & 6) | ((row ^ (row >> 3)) & 1);
-}
-
-template <int SEL_X, int SEL_Y>
-__device__ __forceinline__ v16f_t mfma_fp4(const uint4& x, const uint4& y, v16f_t c, uint32_t sx,
-                                           uint32_t sy) {
-  const v8i_t xv = {(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
-  const v8i_t yv = {(int)y.x, (int)y.y, (int)y.z, (int)y.w, 0, 0, 0, 0};
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(xv, yv, c, 4, 4, SEL_X, (int)sx, SEL_Y,
-                                                         (int)sy);
-}
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  const __bf16 l = (__bf16)lo;
-  const __bf16 h = (__bf16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, l) |
-         ((uint32_t)__builtin_bit_cast(uint16_t, h) << 16);
-}
 
 // Map the hardware workgroup id to a (tile_m, tile_n) pair.
 __device__ __forceinline__ void tile_of(int pid, int tiles_m, int tiles_n, int& tm, int& tn) {
@@ -154,23 +131,6 @@ struct Ctx {
   uint32_t s_sel;           // byte-permute selector picking this lane half's bytes
   int wave;
 };
-
-// Global -> LDS copies. lds is the wave-uniform LDS byte address of the
-// destination; lane i's bytes land at lds + size * i. Inline assembly, so
-// that the compiler, which cannot tell the LDS buffers apart, adds no wait
-// for these loads before LDS reads: every wait on them is an explicit one.
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(g), "s"(lds) : "m0");
-}
-__device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
-               :: "v"(g), "s"(lds) : "m0");
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
 
 // Code load q (0..3) of this wave's share of K step kt: tile rows
 // 32 w + 8 q .. +7, 128 bytes each. Lane i lands at row 32 w + 8 q + i / 8,

@@ -1,0 +1,202 @@
+// Block-scaled MXFP4 x MXFP4 GEMM (TN) for few rows of A: decode-shaped
+// problems such as M = 32 against a large N x K weight, where the work is
+// streaming B from HBM once and the MFMAs are nearly idle.
+//
+// Same contract and arithmetic as the tile kernel (the MXFP4 hipBLASLt path
+// of "Integrate MXFP4 hipblaslt GEMM support", ROCm/TransformerEngine #697,
+// Changes list: TN, plain UE8M0 block-32 scales, BF16/FP32 out, K % 256,
+// M/N % 32, no bias, beta = 0); only the work split differs.
+//
+// Work split. One workgroup of 8 waves owns a 32 x 32 tile of C (32 rows of
+// A, 32 rows of B), so M = 32 already gives N / 32 workgroups. The K range
+// is split between the waves (intra-workgroup split-K): wave w takes K steps
+// [w S / 8, (w + 1) S / 8) of the S = K / 256, accumulates a 32 x 32 fp32
+// partial with one v_mfma_scale_f32_32x32x64_f8f6f4 per 64-wide K slice, and
+// the 8 partials are summed in LDS, in wave order, before the epilogue.
+//
+// Data movement. Each wave streams its K range through a private two-slot
+// LDS ring with global_load_lds: per 256-wide K step, 32 rows x 128 bytes of
+// A codes and of B codes (four wave instructions each, 8 whole cache lines
+// per instruction) and 32 rows x 8 bytes of A and B scales (one dword
+// instruction each). Two steps are in flight per wave (16 KiB), 128 KiB per
+// workgroup, enough to cover HBM latency with one workgroup per CU.
+//
+// K order inside a step. The MFMA only needs A and B to agree on which K
+// block a lane holds, so lane half h of slice s takes block 4 h + s of the
+// step's 8 blocks: its scale bytes for the 4 slices are then one dword of
+// its row (dword h), byte s picked by op_sel, and its code chunk 4 h + s is
+// read from the XOR-swizzled 128-byte LDS row.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gfx950.h"
+#include "kernels.h"
+
+namespace mxfp4 {
+namespace {
+
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kTile = 32;                             // rows of A and of B per workgroup
+constexpr int kStepK = 256;                           // K per ring slot
+constexpr int kRowBytes = kStepK / 2;                 // code bytes per row per step
+constexpr int kCodeBytes = kTile * kRowBytes;         // 4 KiB per operand per slot
+constexpr int kScaleRow = kStepK / 32;                // scale bytes per row per step
+constexpr int kScaleBytes = kTile * kScaleRow;        // 256 B per operand per slot
+// Slot layout: [A codes][B codes][A scales][B scales].
+constexpr int kSlotB = kCodeBytes;
+constexpr int kSlotAs = 2 * kCodeBytes;
+constexpr int kSlotBs = 2 * kCodeBytes + kScaleBytes;
+constexpr int kSlotBytes = 2 * kCodeBytes + 2 * kScaleBytes;
+constexpr int kWaveBytes = 2 * kSlotBytes;
+constexpr int kLdsBytes = kWaves * kWaveBytes;        // 136 KiB
+constexpr int kLoadsPerStep = 10;                     // 4 + 4 code, 2 scale instructions
+
+static_assert(kWaves * kTile * kTile * 4 <= kLdsBytes, "reduction buffer fits the ring");
+
+// Per-lane global offsets of one wave's loads.
+struct Lanes {
+  uint32_t code[2];  // code DMA, rows at 0 and 8 mod 16 (swizzle applied at the source)
+  uint32_t scale;    // scale DMA: row lane / 2, dword lane % 2
+};
+
+// Issue the loads of K step `st` into the slot at LDS address `slot`.
+// Code instruction q fills tile rows 8 q .. 8 q + 7: lane i lands at row
+// 8 q + i / 8, physical chunk i % 8, and so fetches logical chunk
+// (i % 8) ^ swizzle(row). The scale instruction lands lane i's dword at
+// 4 i: [row][dword 0, 1].
+__device__ __forceinline__ void issue_step(const uint8_t* a, const uint8_t* b, const uint8_t* as,
+                                           const uint8_t* bs, int row_bytes, const Lanes& ln,
+                                           uint32_t slot, int st) {
+  const int kb = st * kRowBytes;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    dma16(a + (int64_t)(8 * q) * row_bytes + kb + ln.code[q & 1], slot + q * 1024);
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    dma16(b + (int64_t)(8 * q) * row_bytes + kb + ln.code[q & 1], slot + kSlotB + q * 1024);
+  dma4(as + st * kScaleRow + ln.scale, slot + kSlotAs);
+  dma4(bs + st * kScaleRow + ln.scale, slot + kSlotBs);
+}
+
+template <bool kOutFp32>
+__global__ __launch_bounds__(kThreads) void gemm_skinny_kernel(
+    const uint8_t* __restrict__ A, const uint8_t* __restrict__ As,
+    const uint8_t* __restrict__ B, const uint8_t* __restrict__ Bs, int N, int K,
+    void* __restrict__ C) {
+  __shared__ __align__(16) uint8_t lds[kLdsBytes];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int r = lane & 31;
+  const int h = lane >> 5;
+  const int n0 = blockIdx.x * kTile;
+  const int m0 = blockIdx.y * kTile;
+  const int row_bytes = K / 2;
+  const int srow_bytes = K / 32;
+  const int steps = K / kStepK;
+  const int st_begin = wave * steps / kWaves;
+  const int nst = (wave + 1) * steps / kWaves - st_begin;
+
+  Lanes ln;
+#pragma unroll
+  for (int par = 0; par < 2; ++par) {
+    const int prow = lane >> 3;
+    ln.code[par] =
+        (uint32_t)(prow * row_bytes + (((lane & 7) ^ chunk_swizzle(8 * par + prow)) << 4));
+  }
+  ln.scale = (uint32_t)((lane >> 1) * srow_bytes + 4 * (lane & 1));
+
+  const uint8_t* a = A + (int64_t)m0 * row_bytes;
+  const uint8_t* b = B + (int64_t)n0 * row_bytes;
+  const uint8_t* as = As + (int64_t)m0 * srow_bytes;
+  const uint8_t* bs = Bs + (int64_t)n0 * srow_bytes;
+  uint8_t* ring = lds + wave * kWaveBytes;
+  const uint32_t ring_lds = __builtin_amdgcn_readfirstlane(lds_addr(ring));
+
+  // Fragment offsets within a slot: logical chunk 4 h + s of row r.
+  const int swz = chunk_swizzle(r);
+  const int frag_row = r * kRowBytes;
+  const int scale_off = r * kScaleRow + 4 * h;
+
+  v16f_t acc = v16f_t{};
+  if (nst > 0) issue_step(a, b, as, bs, row_bytes, ln, ring_lds, st_begin);
+  if (nst > 1) issue_step(a, b, as, bs, row_bytes, ln, ring_lds + kSlotBytes, st_begin + 1);
+  for (int i = 0; i < nst; ++i) {
+    // Step i has landed once at most the next step's loads are outstanding.
+    if (i + 1 < nst)
+      asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kLoadsPerStep) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    const uint8_t* slot = ring + (i & 1) * kSlotBytes;
+    uint4 fa[4], fb[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int off = frag_row + (((4 * h + s) ^ swz) << 4);
+      fa[s] = *reinterpret_cast<const uint4*>(slot + off);
+      fb[s] = *reinterpret_cast<const uint4*>(slot + kSlotB + off);
+    }
+    const uint32_t sa = *reinterpret_cast<const uint32_t*>(slot + kSlotAs + scale_off);
+    const uint32_t sb = *reinterpret_cast<const uint32_t*>(slot + kSlotBs + scale_off);
+    if (i + 2 < nst) {
+      // The slot is refilled only after every read of it has returned.
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      issue_step(a, b, as, bs, row_bytes, ln, ring_lds + (i & 1) * kSlotBytes, st_begin + i + 2);
+    }
+    acc = mfma_fp4<0, 0>(fb[0], fa[0], acc, sb, sa);
+    acc = mfma_fp4<1, 1>(fb[1], fa[1], acc, sb, sa);
+    acc = mfma_fp4<2, 2>(fb[2], fa[2], acc, sb, sa);
+    acc = mfma_fp4<3, 3>(fb[3], fa[3], acc, sb, sa);
+  }
+
+  // Split-K reduce. B is the MFMA's first operand, so accumulator register
+  // 4 q + t of lane l holds C[m0 + l % 32][n0 + 8 q + 4 (l / 32) + t].
+  // Every wave's loads have completed (vmcnt(0) on its last step).
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(lds);
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    *reinterpret_cast<float4*>(red + wave * 1024 + q * 256 + lane * 4) =
+        make_float4(acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]);
+  __syncthreads();
+  if (threadIdx.x < 256) {
+    const int q = threadIdx.x >> 6;
+    float4 sum = *reinterpret_cast<const float4*>(red + q * 256 + lane * 4);
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) {
+      const float4 v = *reinterpret_cast<const float4*>(red + w * 1024 + q * 256 + lane * 4);
+      sum.x += v.x;
+      sum.y += v.y;
+      sum.z += v.z;
+      sum.w += v.w;
+    }
+    const int m = m0 + r;
+    const int n = n0 + 8 * q + 4 * h;
+    if constexpr (kOutFp32) {
+      *reinterpret_cast<float4*>(static_cast<float*>(C) + (int64_t)m * N + n) = sum;
+    } else {
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(C) + (int64_t)m * N + n) =
+          make_uint2(pack_bf16x2(sum.x, sum.y), pack_bf16x2(sum.z, sum.w));
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gemm_skinny(const void* A, const void* As, const void* B, const void* Bs, int M,
+                              int N, int K, bool out_fp32, void* C, hipStream_t stream) {
+  const dim3 grid(N / kTile, M / kTile);
+  const auto* a = static_cast<const uint8_t*>(A);
+  const auto* as = static_cast<const uint8_t*>(As);
+  const auto* b = static_cast<const uint8_t*>(B);
+  const auto* bs = static_cast<const uint8_t*>(Bs);
+  if (out_fp32)
+    hipLaunchKernelGGL(gemm_skinny_kernel<true>, grid, dim3(kThreads), 0, stream, a, as, b, bs, N,
+                       K, C);
+  else
+    hipLaunchKernelGGL(gemm_skinny_kernel<false>, grid, dim3(kThreads), 0, stream, a, as, b, bs,
+                       N, K, C);
+  return hipGetLastError();
+}
+
+}  // namespace mxfp4

@@ -16,6 +16,12 @@ hipError_t launch_quantize(const void* x_bf16, int64_t nblocks, void* codes, voi
 hipError_t launch_gemm(const void* A, const void* As, const void* B, const void* Bs, int M,
                        int N, int K, bool out_fp32, void* C, hipStream_t stream);
 
+// Same contract, for M up to kSkinnyMaxM: one 32 x 32 tile of C per
+// workgroup, K split between its waves.
+constexpr int kSkinnyMaxM = 128;
+hipError_t launch_gemm_skinny(const void* A, const void* As, const void* B, const void* Bs,
+                              int M, int N, int K, bool out_fp32, void* C, hipStream_t stream);
+
 // One-time per-device set-up of kernel attributes (large LDS allocations).
 hipError_t init_kernels_for_current_device();
 

@@ -77,7 +77,12 @@ int mxfp4_quantize_async(const void* x_bf16, int64_t M, int64_t K, void* codes_o
  * A_codes [M, K/2], B_codes [N, K/2]: 16-byte aligned
  * A_scales [M, K/32], B_scales [N, K/32]: 4-byte aligned
  * C [M, N] row-major BF16 or FP32: 16-byte aligned
- * M, N, K <= 2^31 - 1 and each buffer < 2^40 bytes. */
+ * M, N <= 2^31 - 1, K <= 2^24, and each buffer < 2^40 bytes; otherwise
+ * MXFP4_EINVAL (or MXFP4_EALIGN for alignment) and nothing is launched.
+ * M <= 128 runs a split-K kernel (one 32 x 32 tile of C per workgroup, the K
+ * range split between its waves and summed in LDS in a fixed order); larger
+ * M runs 256 x 256 tiles. Both give the same results up to fp32 summation
+ * order. */
 int mxfp4_gemm(const void* A_codes, const void* A_scales, const void* B_codes,
                const void* B_scales, int64_t M, int64_t N, int64_t K, int out_dtype,
                void* C, void* stream);

@@ -46,7 +46,7 @@ def test_strerror_texts():
 @pytest.mark.parametrize("M,N,K", [
     (0, 32, 256), (32, 0, 256), (32, 32, 0), (-32, 32, 256),
     (33, 32, 256), (32, 48, 256), (32, 32, 128), (32, 32, 384),
-    (1 << 31, 32, 256), (32, 32, (1 << 31) + 256),
+    (1 << 31, 32, 256), (32, 32, (1 << 31) + 256), (32, 32, (1 << 24) + 256),
 ])
 def test_gemm_rejects_bad_sizes(M, N, K):
     assert mx.mxfp4_gemm(P16, P16, P16, P16, M, N, K, mx.OUT_BF16, P16, None) == EINVAL

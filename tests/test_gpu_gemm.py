@@ -8,6 +8,10 @@ BF16 step of the oracle rounded to BF16 (with the near-cancellation reading
 documented in oracle/compare.py). The non-zero count check guards against the
 silent all-zeros failure reported on "feat(ck-tile): aquant GEMM TE to
 dispatcher bridge" (rocm-libraries #9980, GPU validation).
+
+The library runs M <= 128 on the split-K kernel and larger M on the 256 x 256
+tile kernel, so each layout case runs at M = 32 (or the case's own small M)
+and again with its rows repeated past 128.
 """
 
 import numpy as np
@@ -31,41 +35,54 @@ def _assert_not_silent_zeros(got, c_ref, s_ref):
     assert np.count_nonzero(got[significant]) == int(significant.sum())
 
 
+# Row counts that reach each kernel: 32 -> split-K kernel (M <= 128),
+# 160 -> tile kernel.
+KERNEL_ROWS = [32, 160]
+
+
+def _rep(x, rows):
+    """Repeat a 32-row operand (or expected C) down to `rows` rows."""
+    return np.tile(x, (rows // x.shape[0],) + (1,) * (x.ndim - 1))
+
+
 def _gemm(Ac, As, Bc, Bs, out_dtype):
     out = mx.gemm(u8_to_dev(Ac), u8_to_dev(As), u8_to_dev(Bc), u8_to_dev(Bs), out_dtype=out_dtype)
     torch.cuda.synchronize()
     return out
 
 
+@pytest.mark.parametrize("rows", KERNEL_ROWS)
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
-def test_single_tile_random(out_dtype):
+def test_single_tile_random(out_dtype, rows):
     """One 32 x 32 x 256 problem: pins the MFMA operand/scale lane layout."""
-    announce(f"gemm 32x32x256 random {out_dtype}")
-    Ac, Bc = random_codes(32, 256, 1), random_codes(32, 256, 2)
-    As, Bs = random_scales(32, 256, 3), random_scales(32, 256, 4)
+    announce(f"gemm {rows}x32x256 random {out_dtype}")
+    Ac, Bc = random_codes(rows, 256, 1), random_codes(32, 256, 2)
+    As, Bs = random_scales(rows, 256, 3), random_scales(32, 256, 4)
     out = _gemm(Ac, As, Bc, Bs, out_dtype)
     c_ref, s_ref = oracle.gemm(Ac, As, Bc, Bs)
     check_gemm_output(out, c_ref, s_ref)
 
 
-def test_hand_worked_g1_padded():
-    """Q1 block x unit B rows (1 x 32 x 32 by hand), padded to 32 x 32 x 256
+@pytest.mark.parametrize("rows", KERNEL_ROWS)
+def test_hand_worked_g1_padded(rows):
+    """Q1 block x unit B rows (1 x 32 x 32 by hand), padded to rows x 32 x 256
     with zero codes: row 0 of C is the dequantized Q1 block."""
-    announce("gemm G1 padded")
+    announce(f"gemm G1 padded to {rows} rows")
     g = read_golden("q1_block.txt")
-    Ac = np.zeros((32, 128), np.uint8)
+    Ac = np.zeros((rows, 128), np.uint8)
     Ac[0, :16] = [int(v, 16) for v in g["packed"]]
-    As = np.full((32, 8), 127, np.uint8)
+    As = np.full((rows, 8), 127, np.uint8)
     Bc = np.zeros((32, 128), np.uint8)
     for n in range(32):
         Bc[n, n // 2] = 2 << (4 * (n % 2))
-    out = _gemm(Ac, As, Bc, As, torch.float32).cpu().numpy()
+    out = _gemm(Ac, As, Bc, As[:32], torch.float32).cpu().numpy()
     assert out[0].tolist() == [float(v) for v in g["dequant"]]
     assert np.all(out[1:] == 0)
 
 
-def test_hand_worked_g2_g3_g4():
-    announce("gemm G2 G3 G4")
+@pytest.mark.parametrize("rows", KERNEL_ROWS)
+def test_hand_worked_g2_g3_g4(rows):
+    announce(f"gemm G2 G3 G4 at {rows} rows")
     n = np.arange(32)
     m = np.arange(32)[:, None]
     # G2: C = 255 * 2^(n % 3)
@@ -73,13 +90,13 @@ def test_hand_worked_g2_g3_g4():
     As = np.tile(np.arange(123, 131, dtype=np.uint8), (32, 1))
     Bs = (126 + n % 3).astype(np.uint8)[:, None].repeat(8, axis=1)
     for dt in (torch.float32, torch.bfloat16):
-        out = _gemm(A, As, A, Bs, dt).float().cpu().numpy()
-        assert np.array_equal(out, np.tile(255.0 * 2.0 ** (n % 3), (32, 1)))
+        out = _gemm(_rep(A, rows), _rep(As, rows), A, Bs, dt).float().cpu().numpy()
+        assert np.array_equal(out, np.tile(255.0 * 2.0 ** (n % 3), (rows, 1)))
     # G3: nibble pairing, C = 448 everywhere
     s = np.full((32, 8), 127, np.uint8)
-    out = _gemm(np.full((32, 128), 0x13, np.uint8), s, np.full((32, 128), 0x24, np.uint8), s,
-                torch.float32).cpu().numpy()
-    assert np.all(out == 448.0)
+    out = _gemm(_rep(np.full((32, 128), 0x13, np.uint8), rows), _rep(s, rows),
+                np.full((32, 128), 0x24, np.uint8), s, torch.float32).cpu().numpy()
+    assert out.shape == (rows, 32) and np.all(out == 448.0)
     # G4: scale-to-block mapping, C = 2338 * 2^(m%2 + n%4 - 2)
     A = np.zeros((32, 128), np.uint8)
     for j in range(8):
@@ -87,13 +104,17 @@ def test_hand_worked_g2_g3_g4():
     As = (123 + np.arange(8)[None, :] + (np.arange(32) % 2)[:, None]).astype(np.uint8)
     B = np.full((32, 128), 0x22, np.uint8)
     Bs = (125 + n % 4).astype(np.uint8)[:, None].repeat(8, axis=1)
-    out = _gemm(A, As, B, Bs, torch.float32).cpu().numpy()
-    assert np.array_equal(out, 2338.0 * 2.0 ** ((m % 2) + (n[None, :] % 4) - 2))
+    out = _gemm(_rep(A, rows), _rep(As, rows), B, Bs, torch.float32).cpu().numpy()
+    assert np.array_equal(out, _rep(2338.0 * 2.0 ** ((m % 2) + (n[None, :] % 4) - 2), rows))
 
 
 @pytest.mark.parametrize("M,N,K", [(32, 32, 256), (256, 256, 256), (288, 544, 512),
                                    (544, 288, 1024), (64, 800, 768), (512, 96, 2304),
-                                   (800, 1056, 256)])
+                                   (800, 1056, 256), (160, 64, 512),
+                                   # split-K kernel: K steps not a multiple of its 8
+                                   # waves, a single step (7 idle waves), long K
+                                   (96, 320, 2304), (128, 64, 256), (128, 288, 768),
+                                   (32, 96, 14336), (64, 2080, 7936)])
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
 def test_random_operands_many_tiles(M, N, K, out_dtype):
     """Uniform random code bytes (every code, both signs) and scales 117..137,
@@ -107,10 +128,11 @@ def test_random_operands_many_tiles(M, N, K, out_dtype):
     _assert_not_silent_zeros(out.float().cpu().numpy(), c_ref, s_ref)
 
 
-def test_wide_scale_range():
+@pytest.mark.parametrize("M", [96, 288])
+def test_wide_scale_range(M):
     """Scales 100..150 on both sides: products span 2^-54 .. 2^46."""
-    announce("gemm wide scale range")
-    M, N, K = 96, 160, 1280
+    announce(f"gemm wide scale range M={M}")
+    N, K = 160, 1280
     Ac, Bc = random_codes(M, K, 31), random_codes(N, K, 32)
     As, Bs = random_scales(M, K, 33, 100, 150), random_scales(N, K, 34, 100, 150)
     out = _gemm(Ac, As, Bc, Bs, torch.float32)
@@ -118,11 +140,12 @@ def test_wide_scale_range():
     check_gemm_output(out, c_ref, s_ref)
 
 
-def test_scale_doubling_is_exact():
+@pytest.mark.parametrize("M", [64, 288])
+def test_scale_doubling_is_exact(M):
     """Adding 1 to every A scale of one row doubles that C row bit for bit
     (power-of-two scaling commutes with fp32 rounding) and leaves the others."""
-    announce("gemm scale doubling invariant")
-    M, N, K = 64, 288, 1024
+    announce(f"gemm scale doubling invariant M={M}")
+    N, K = 288, 1024
     Ac, Bc = random_codes(M, K, 41), random_codes(N, K, 42)
     As, Bs = random_scales(M, K, 43), random_scales(N, K, 44)
     c0 = _gemm(Ac, As, Bc, Bs, torch.float32).cpu().numpy()
@@ -133,9 +156,10 @@ def test_scale_doubling_is_exact():
     assert np.array_equal(np.delete(c1, 17, axis=0), np.delete(c0, 17, axis=0))
 
 
-def test_output_written_exactly_in_bounds():
-    announce("gemm canary")
-    M, N, K = 288, 320, 512
+@pytest.mark.parametrize("M", [96, 288])
+def test_output_written_exactly_in_bounds(M):
+    announce(f"gemm canary M={M}")
+    N, K = 320, 512
     Ac, Bc = random_codes(M, K, 51), random_codes(N, K, 52)
     As, Bs = random_scales(M, K, 53), random_scales(N, K, 54)
     pad = 4096
@@ -149,9 +173,10 @@ def test_output_written_exactly_in_bounds():
     check_gemm_output(out, c_ref, s_ref)
 
 
-def test_side_stream():
-    announce("gemm on a side stream")
-    M, N, K = 256, 512, 768
+@pytest.mark.parametrize("M", [64, 256])
+def test_side_stream(M):
+    announce(f"gemm on a side stream M={M}")
+    N, K = 512, 768
     Ac, Bc = random_codes(M, K, 61), random_codes(N, K, 62)
     As, Bs = random_scales(M, K, 63), random_scales(N, K, 64)
     args = [u8_to_dev(t) for t in (Ac, As, Bc, Bs)]
