@@ -16,8 +16,9 @@ Prints one JSON line:
                C) / mean GEMM launch time, with B rotated through enough
                copies that it is read from HBM each step
   cpu_baseline the float64 NumPy oracle on a bounded sample of the same
-               workload (a 4096 x 8192 block of C over the full K, including
-               the oracle's quantize of the 12288 operand rows it needs)
+               workload (up to an 8192 x 8192 block of C over the full K, the
+               whole square GEMM, including the oracle's quantize of the
+               operand rows it needs)
 """
 
 import argparse
@@ -90,7 +91,7 @@ def copy_calibration(mib):
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}), flush=True)
 
 
-def cpu_baseline(a_bits, b_bits, K, rows=4096, cols=8192):
+def cpu_baseline(a_bits, b_bits, K, rows=8192, cols=8192):
     import oracle
     cores = len(os.sched_getaffinity(0))
     rows = min(rows, a_bits.shape[0])
