@@ -23,7 +23,12 @@
 //
 // Data movement. A K step is 256 wide: 128 bytes of codes per row (one
 // cache line), four MFMA K slices. Code tiles go global -> LDS with
-// global_load_lds_dwordx4, each wave instruction filling 8 rows x 128 bytes.
+// global_load_lds_dwordx4, each wave instruction filling 8 rows x 128 bytes,
+// issued in pairs from a wave-uniform SGPR base and per-lane offsets
+// prepared once per tile. Every non-MFMA instruction in the K loop costs
+// MFMA issue time once there are more than about two per MFMA, so the loop
+// keeps address arithmetic out: fragment reads use a per-lane register plus
+// an immediate offset, and DMA addresses need no per-lane arithmetic.
 // LDS holds two K steps (2 x 64 KiB) and a double buffer of scale words (one
 // word per row per 128 K, 8 half-steps per chunk, 2 x 16 KiB): 160 KiB.
 //   Step T, phases p = 0..3 (slice p of step T on the MFMAs):
@@ -76,9 +81,12 @@ constexpr int kChunk = 8;
 constexpr int kChunkSteps = kChunk / 2;
 constexpr int kChunkBytes = kTileM * kChunk * 4;  // 8 KiB per operand
 
-struct __align__(16) Slot {
-  uint8_t a[kTileBytes];
-  uint8_t b[kTileBytes];
+// The two K-step slots of each operand: a[S] and b[S] for S = 0, 1. Keeping
+// both A slots within 64 KiB lets every fragment read use a per-lane
+// register plus an immediate offset (slot, tile).
+struct __align__(16) Tiles {
+  uint8_t a[2][kTileBytes];
+  uint8_t b[2][kTileBytes];
 };
 
 __device__ __forceinline__ void tile_of(int pid, int tiles_m, int tiles_n, int& tm, int& tn) {
@@ -117,9 +125,16 @@ struct Ctx {
   int row0, col0, M, N;
   int klast, hlast;
   uint32_t code_lane[2];  // per-lane code DMA offset for row groups at 16 r, 16 r + 8
+  const uint8_t* tile_a;  // wave-uniform code bases of this tile, less kDmaBias
+  const uint8_t* tile_b;
+  uint32_t off_a[8];      // per-lane offsets of code loads q = 0..7 from those bases
+  uint32_t off_b[8];
   int scale_lane;          // 32 (lane % 4) + lane / 32
   int scale_t;             // (lane / 4) % 8: the scale DMA lane's stored half-step
   int a_base, b_base;      // fragment row offsets (bytes) of this lane
+  uint32_t fa_off[4];      // a_base + (32 sl ^ frag_x) for slices sl = 0..3
+  uint32_t fb_off[4];      // b_base + (32 sl ^ frag_x)
+  uint32_t soff[2][4][2];  // scale DMA pair (operand, pair p): per-lane offsets of parts 2p, 2p+1
   uint32_t frag_x;         // chunk swizzle of this lane's rows, pre-shifted, with h
   int s_off, sb_off;       // the lane's scale words in a chunk: 128 (32 wy + r), 128 (32 wx + r)
   int s_x;                 // half-step XOR key of the lane's scale rows: (r >> 1) & 7
@@ -133,18 +148,35 @@ struct Ctx {
 // depends on the row mod 16, so a lane needs two offsets. The 8 rows of one
 // load lie wholly below M (or N) or wholly above it (M % 32 == 0); loads
 // above it re-read the last 8 rows: computed, never stored.
-__device__ __forceinline__ const uint8_t* code_src(const Ctx& c, const uint8_t* base, int origin,
-                                                   int rows, int q, int kt) {
-  const int grow = min(origin + 64 * c.wave + 8 * q, rows - 8);
-  return base + (int64_t)grow * c.row_bytes + kt * kRowBytes + c.code_lane[q & 1];
+// Code loads go in pairs q, q + 1 (q even) of one operand: a wave-uniform
+// base in SGPRs, a per-lane 32-bit offset, and M0 = the LDS address of load
+// 4 (q / 4); the instruction's immediate offset (q % 4) * 1024 moves both the
+// global and the LDS address. The per-lane offsets carry kDmaBias to stay
+// non-negative after the immediate is taken off.
+constexpr int kDmaBias = 3072;
+
+template <int Q0>
+__device__ __forceinline__ void dma_pair(const uint8_t* base, uint32_t off0, uint32_t off1,
+                                         uint32_t m0) {
+  asm volatile(
+      "s_mov_b32 m0, %3\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %2 offset:%4\n\t"
+      "global_load_lds_dwordx4 %1, %2 offset:%5"
+      :: "v"(off0), "v"(off1), "s"(base), "s"(m0), "n"((Q0 % 4) * 1024),
+         "n"(((Q0 + 1) % 4) * 1024)
+      : "m0");
 }
-__device__ __forceinline__ void load_a(const Ctx& c, Slot& s, int q, int kt) {
-  const uint32_t l = __builtin_amdgcn_readfirstlane(lds_addr(s.a) + c.wave * 8192 + q * 1024);
-  dma16(code_src(c, c.A, c.row0, c.M, q, kt), l);
+template <int Q0, int S>
+__device__ __forceinline__ void load_a2(const Ctx& c, Tiles& t, int kt) {
+  const uint32_t m0 =
+      __builtin_amdgcn_readfirstlane(lds_addr(t.a[S]) + c.wave * 8192 + (Q0 / 4) * 4096);
+  dma_pair<Q0>(c.tile_a + kt * kRowBytes, c.off_a[Q0], c.off_a[Q0 + 1], m0);
 }
-__device__ __forceinline__ void load_b(const Ctx& c, Slot& s, int q, int kt) {
-  const uint32_t l = __builtin_amdgcn_readfirstlane(lds_addr(s.b) + c.wave * 8192 + q * 1024);
-  dma16(code_src(c, c.B, c.col0, c.N, q, kt), l);
+template <int Q0, int S>
+__device__ __forceinline__ void load_b2(const Ctx& c, Tiles& t, int kt) {
+  const uint32_t m0 =
+      __builtin_amdgcn_readfirstlane(lds_addr(t.b[S]) + c.wave * 8192 + (Q0 / 4) * 4096);
+  dma_pair<Q0>(c.tile_b + kt * kRowBytes, c.off_b[Q0], c.off_b[Q0 + 1], m0);
 }
 
 // Scale part u (0..7) of operand X (0 = A, 1 = B) of chunk `chunk`: words
@@ -165,6 +197,44 @@ __device__ __forceinline__ void load_scale_part(const Ctx& c, uint8_t* buf, int 
   dma4(base + (int64_t)row * c.scale_row_bytes + hs * 4, dst);
 }
 
+// Scale parts 2p, 2p + 1 of operand X for chunk `chunk` as one DMA pair:
+// their words sit 1024 bytes apart in the chunk buffer, and their per-lane
+// offsets (prepared per tile, with kScaleBias) are relative to part 2p's
+// clamped base row. Only for chunks whose 8 half-steps all lie within K; the
+// last chunk of a K that is not a multiple of 1024 takes load_scale_part.
+constexpr int kScaleBias = 1024;
+template <int X, int PP>
+__device__ __forceinline__ void load_scale_pair(const Ctx& c, uint8_t* buf, int chunk) {
+  const int origin = X == 0 ? c.row0 : c.col0;
+  const int rows = X == 0 ? c.M : c.N;
+  const uint8_t* base = X == 0 ? c.As : c.Bs;
+  const int row_c = min(origin + 128 * (PP / 2) + 16 * (PP % 2) + 2 * c.wave, rows - 1);
+  // The last steps prefetch chunks past the end of K: those re-read the last
+  // chunk (never used) instead of running past the scale rows.
+  const int chunk_c = min(chunk, c.hlast / kChunk);
+  const uint8_t* sbase =
+      base + (int64_t)row_c * c.scale_row_bytes + kChunk * 4 * chunk_c - kScaleBias;
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr(buf) + X * kChunkBytes +
+                                                     4 * (256 * (2 * PP) + 64 * c.wave));
+  asm volatile(
+      "s_mov_b32 m0, %3\n\ts_nop 0\n\t"
+      "global_load_lds_dword %0, %2\n\t"
+      "global_load_lds_dword %1, %2 offset:1024"
+      :: "v"(c.soff[X][PP][0]), "v"(c.soff[X][PP][1]), "s"(sbase), "s"(m0)
+      : "m0");
+}
+
+// kFull: K is a multiple of 1024, so every chunk is whole.
+template <bool kFull, int X, int PP>
+__device__ __forceinline__ void load_scales2(const Ctx& c, uint8_t* buf, int chunk) {
+  if constexpr (kFull) {
+    load_scale_pair<X, PP>(c, buf, chunk);
+  } else {
+    load_scale_part<X, 2 * PP>(c, buf, chunk);
+    load_scale_part<X, 2 * PP + 1>(c, buf, chunk);
+  }
+}
+
 // The lane's scale operands of half-step t (0..7) of a chunk buffer.
 __device__ __forceinline__ void read_half_scales(const Ctx& c, const uint8_t* buf, int t,
                                                  HalfScales& sc) {
@@ -182,11 +252,15 @@ __device__ __forceinline__ void read_half_scales(const Ctx& c, const uint8_t* bu
 __device__ __forceinline__ int frag_off(const Ctx& c, int sl) {
   return (int)((uint32_t)(32 * sl) ^ c.frag_x);
 }
-__device__ __forceinline__ void read_frag_a(const Ctx& c, const Slot& s, int sl, int i, uint4& f) {
-  f = *reinterpret_cast<const uint4*>(&s.a[c.a_base + frag_off(c, sl) + i * 32 * kRowBytes]);
+template <int S>
+__device__ __forceinline__ void read_frag_a(const Ctx& c, const Tiles& t, int sl, int i, uint4& f) {
+  f = *reinterpret_cast<const uint4*>(&t.a[0][0] + c.fa_off[sl] + S * kTileBytes +
+                                      i * 32 * kRowBytes);
 }
-__device__ __forceinline__ void read_frag_b(const Ctx& c, const Slot& s, int sl, int j, uint4& f) {
-  f = *reinterpret_cast<const uint4*>(&s.b[c.b_base + frag_off(c, sl) + j * 32 * kRowBytes]);
+template <int S>
+__device__ __forceinline__ void read_frag_b(const Ctx& c, const Tiles& t, int sl, int j, uint4& f) {
+  f = *reinterpret_cast<const uint4*>(&t.b[0][0] + c.fb_off[sl] + S * kTileBytes +
+                                      j * 32 * kRowBytes);
 }
 
 // The four MFMAs of A tile row I of one K slice.
@@ -212,8 +286,8 @@ __device__ __forceinline__ void step_barrier() {
 // T+1: A rows of loads 4..7 and all of B in phases 0-1 (A loads 0..3 came in
 // phase 3 of step T-1). Phase 3 issues step T+2's A loads 0..3 into `cur`
 // and scale parts 2P, 2P+1 of both operands for chunk (T+1)/4 + 1.
-template <int P>
-__device__ __forceinline__ void k_step(const Ctx& c0, Slot& cur, Slot& oth,
+template <bool kFull, int P, int S>
+__device__ __forceinline__ void k_step(const Ctx& c0, Tiles& tl,
                                        uint8_t (*chunks)[2 * kChunkBytes], v16f_t (&acc)[4][4],
                                        Frags& fa, Frags& fb, HalfScales& sc0, HalfScales& sc1,
                                        int T) {
@@ -221,73 +295,65 @@ __device__ __forceinline__ void k_step(const Ctx& c0, Slot& cur, Slot& oth,
   // compiler recomputes the addresses built on them instead of holding every
   // one of them in a register across the loop.
   Ctx c = c0;
-  asm volatile("" : "+v"(c.code_lane[0]), "+v"(c.code_lane[1]), "+v"(c.scale_lane),
-               "+v"(c.scale_t));
-  asm volatile("" : "+v"(c.a_base), "+v"(c.b_base), "+v"(c.frag_x), "+v"(c.s_off),
-               "+v"(c.sb_off));
+  asm volatile("" : "+v"(c.scale_lane), "+v"(c.scale_t));
+  asm volatile("" : "+v"(c.s_off), "+v"(c.sb_off), "+v"(c.s_x), "+v"(c.s_sel));
   const int kb = min(T + 1, c.klast);
   // Phase 0: slice 0; read slice 1.
   mma_row<0, 0>(acc, fa, sc0);
-  read_frag_b(c, cur, 1, 0, fb.b[0]);
-  read_frag_b(c, cur, 1, 1, fb.b[1]);
-  load_a(c, oth, 4, kb);
-  load_a(c, oth, 5, kb);
+  read_frag_b<S>(c, tl, 1, 0, fb.b[0]);
+  read_frag_b<S>(c, tl, 1, 1, fb.b[1]);
+  load_a2<4, 1 - S>(c, tl, kb);
   MXFP4_FENCE();
   mma_row<0, 1>(acc, fa, sc0);
-  read_frag_b(c, cur, 1, 2, fb.b[2]);
-  read_frag_b(c, cur, 1, 3, fb.b[3]);
-  load_a(c, oth, 6, kb);
-  load_a(c, oth, 7, kb);
+  read_frag_b<S>(c, tl, 1, 2, fb.b[2]);
+  read_frag_b<S>(c, tl, 1, 3, fb.b[3]);
+  load_a2<6, 1 - S>(c, tl, kb);
   MXFP4_FENCE();
   mma_row<0, 2>(acc, fa, sc0);
-  read_frag_a(c, cur, 1, 0, fb.a[0]);
-  read_frag_a(c, cur, 1, 1, fb.a[1]);
-  load_b(c, oth, 0, kb);
-  load_b(c, oth, 1, kb);
+  read_frag_a<S>(c, tl, 1, 0, fb.a[0]);
+  read_frag_a<S>(c, tl, 1, 1, fb.a[1]);
+  load_b2<0, 1 - S>(c, tl, kb);
   MXFP4_FENCE();
   mma_row<0, 3>(acc, fa, sc0);
-  read_frag_a(c, cur, 1, 2, fb.a[2]);
-  read_frag_a(c, cur, 1, 3, fb.a[3]);
-  load_b(c, oth, 2, kb);
-  load_b(c, oth, 3, kb);
+  read_frag_a<S>(c, tl, 1, 2, fb.a[2]);
+  read_frag_a<S>(c, tl, 1, 3, fb.a[3]);
+  load_b2<2, 1 - S>(c, tl, kb);
   MXFP4_FENCE();
   // Phase 1: slice 1; read slice 2.
   mma_row<1, 0>(acc, fb, sc0);
-  read_frag_b(c, cur, 2, 0, fa.b[0]);
-  read_frag_b(c, cur, 2, 1, fa.b[1]);
-  load_b(c, oth, 4, kb);
+  read_frag_b<S>(c, tl, 2, 0, fa.b[0]);
+  read_frag_b<S>(c, tl, 2, 1, fa.b[1]);
+  load_b2<4, 1 - S>(c, tl, kb);
   MXFP4_FENCE();
   mma_row<1, 1>(acc, fb, sc0);
-  read_frag_b(c, cur, 2, 2, fa.b[2]);
-  read_frag_b(c, cur, 2, 3, fa.b[3]);
-  load_b(c, oth, 5, kb);
+  read_frag_b<S>(c, tl, 2, 2, fa.b[2]);
+  read_frag_b<S>(c, tl, 2, 3, fa.b[3]);
   MXFP4_FENCE();
   mma_row<1, 2>(acc, fb, sc0);
-  read_frag_a(c, cur, 2, 0, fa.a[0]);
-  read_frag_a(c, cur, 2, 1, fa.a[1]);
-  load_b(c, oth, 6, kb);
+  read_frag_a<S>(c, tl, 2, 0, fa.a[0]);
+  read_frag_a<S>(c, tl, 2, 1, fa.a[1]);
+  load_b2<6, 1 - S>(c, tl, kb);
   MXFP4_FENCE();
   mma_row<1, 3>(acc, fb, sc0);
-  read_frag_a(c, cur, 2, 2, fa.a[2]);
-  read_frag_a(c, cur, 2, 3, fa.a[3]);
-  load_b(c, oth, 7, kb);
+  read_frag_a<S>(c, tl, 2, 2, fa.a[2]);
+  read_frag_a<S>(c, tl, 2, 3, fa.a[3]);
   MXFP4_FENCE();
   // Phase 2: slice 2; read slice 3.
   mma_row<2, 0>(acc, fa, sc1);
-  read_frag_b(c, cur, 3, 0, fb.b[0]);
-  read_frag_b(c, cur, 3, 1, fb.b[1]);
+  read_frag_b<S>(c, tl, 3, 0, fb.b[0]);
+  read_frag_b<S>(c, tl, 3, 1, fb.b[1]);
   MXFP4_FENCE();
   mma_row<2, 1>(acc, fa, sc1);
-  read_frag_b(c, cur, 3, 2, fb.b[2]);
-  read_frag_b(c, cur, 3, 3, fb.b[3]);
+  read_frag_b<S>(c, tl, 3, 2, fb.b[2]);
+  read_frag_b<S>(c, tl, 3, 3, fb.b[3]);
   MXFP4_FENCE();
   mma_row<2, 2>(acc, fa, sc1);
-  read_frag_a(c, cur, 3, 0, fb.a[0]);
-  read_frag_a(c, cur, 3, 1, fb.a[1]);
+  read_frag_a<S>(c, tl, 3, 0, fb.a[0]);
+  read_frag_a<S>(c, tl, 3, 1, fb.a[1]);
   MXFP4_FENCE();
   mma_row<2, 3>(acc, fa, sc1);
-  read_frag_a(c, cur, 3, 2, fb.a[2]);
-  read_frag_a(c, cur, 3, 3, fb.a[3]);
+  read_frag_a<S>(c, tl, 3, 2, fb.a[2]);
+  read_frag_a<S>(c, tl, 3, 3, fb.a[3]);
   MXFP4_FENCE();
   step_barrier();
   MXFP4_FENCE();
@@ -298,28 +364,24 @@ __device__ __forceinline__ void k_step(const Ctx& c0, Slot& cur, Slot& oth,
   const int pchunk = (T + 1) / kChunkSteps + 1;
   uint8_t* pbuf = chunks[pchunk & 1];
   mma_row<3, 0>(acc, fb, sc1);
-  read_frag_b(c, oth, 0, 0, fa.b[0]);
-  read_frag_b(c, oth, 0, 1, fa.b[1]);
-  load_a(c, cur, 0, ka);
-  load_scale_part<0, 2 * P>(c, pbuf, pchunk);
-  load_scale_part<1, 2 * P>(c, pbuf, pchunk);
+  read_frag_b<1 - S>(c, tl, 0, 0, fa.b[0]);
+  read_frag_b<1 - S>(c, tl, 0, 1, fa.b[1]);
+  load_a2<0, S>(c, tl, ka);
+  load_scales2<kFull, 0, P>(c, pbuf, pchunk);
   MXFP4_FENCE();
   mma_row<3, 1>(acc, fb, sc1);
-  read_frag_b(c, oth, 0, 2, fa.b[2]);
-  read_frag_b(c, oth, 0, 3, fa.b[3]);
-  load_a(c, cur, 1, ka);
-  load_scale_part<0, 2 * P + 1>(c, pbuf, pchunk);
-  load_scale_part<1, 2 * P + 1>(c, pbuf, pchunk);
+  read_frag_b<1 - S>(c, tl, 0, 2, fa.b[2]);
+  read_frag_b<1 - S>(c, tl, 0, 3, fa.b[3]);
+  load_scales2<kFull, 1, P>(c, pbuf, pchunk);
   MXFP4_FENCE();
   mma_row<3, 2>(acc, fb, sc1);
-  read_frag_a(c, oth, 0, 0, fa.a[0]);
-  read_frag_a(c, oth, 0, 1, fa.a[1]);
-  load_a(c, cur, 2, ka);
+  read_frag_a<1 - S>(c, tl, 0, 0, fa.a[0]);
+  read_frag_a<1 - S>(c, tl, 0, 1, fa.a[1]);
+  load_a2<2, S>(c, tl, ka);
   MXFP4_FENCE();
   mma_row<3, 3>(acc, fb, sc1);
-  read_frag_a(c, oth, 0, 2, fa.a[2]);
-  read_frag_a(c, oth, 0, 3, fa.a[3]);
-  load_a(c, cur, 3, ka);
+  read_frag_a<1 - S>(c, tl, 0, 2, fa.a[2]);
+  read_frag_a<1 - S>(c, tl, 0, 3, fa.a[3]);
   HalfScales n0, n1;
   read_half_scales(c, sbuf, hs % kChunk, n0);
   read_half_scales(c, sbuf, hs % kChunk + 1, n1);
@@ -328,18 +390,20 @@ __device__ __forceinline__ void k_step(const Ctx& c0, Slot& cur, Slot& oth,
   sc1 = n1;
 }
 
-// Issue the loads that start a tile: K step 0 and scale chunk 0 into slot0
+// Issue the loads that start a tile: K step 0 and scale chunk 0 into slot 0
 // and chunks[0].
-__device__ __forceinline__ void issue_tile_head(const Ctx& c0, Slot& slot0,
+__device__ __forceinline__ void issue_tile_head(const Ctx& c0, Tiles& tl,
                                                 uint8_t (*chunks)[2 * kChunkBytes]) {
   Ctx c = c0;
-  asm volatile("" : "+v"(c.code_lane[0]), "+v"(c.code_lane[1]), "+v"(c.scale_lane),
-               "+v"(c.scale_t));
-#pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    load_a(c, slot0, q, 0);
-    load_b(c, slot0, q, 0);
-  }
+  asm volatile("" : "+v"(c.scale_lane), "+v"(c.scale_t));
+  load_a2<0, 0>(c, tl, 0);
+  load_a2<2, 0>(c, tl, 0);
+  load_a2<4, 0>(c, tl, 0);
+  load_a2<6, 0>(c, tl, 0);
+  load_b2<0, 0>(c, tl, 0);
+  load_b2<2, 0>(c, tl, 0);
+  load_b2<4, 0>(c, tl, 0);
+  load_b2<6, 0>(c, tl, 0);
   load_scale_part<0, 0>(c, chunks[0], 0);
   load_scale_part<0, 1>(c, chunks[0], 0);
   load_scale_part<0, 2>(c, chunks[0], 0);
@@ -360,13 +424,12 @@ __device__ __forceinline__ void issue_tile_head(const Ctx& c0, Slot& slot0,
 
 // What phase 3 of step "-1" would have issued: A loads 0..3 of step 1 and
 // parts 0, 1 of chunk 1. Exactly 8 loads: the tile's first wait is vmcnt(8).
-__device__ __forceinline__ void issue_tile_tail(const Ctx& c0, Slot& slot1,
+__device__ __forceinline__ void issue_tile_tail(const Ctx& c0, Tiles& tl,
                                                 uint8_t (*chunks)[2 * kChunkBytes]) {
   Ctx c = c0;
-  asm volatile("" : "+v"(c.code_lane[0]), "+v"(c.code_lane[1]), "+v"(c.scale_lane),
-               "+v"(c.scale_t));
-#pragma unroll
-  for (int q = 0; q < 4; ++q) load_a(c, slot1, q, min(1, c.klast));
+  asm volatile("" : "+v"(c.scale_lane), "+v"(c.scale_t));
+  load_a2<0, 1>(c, tl, min(1, c.klast));
+  load_a2<2, 1>(c, tl, min(1, c.klast));
   load_scale_part<0, 0>(c, chunks[1], 1);
   load_scale_part<1, 0>(c, chunks[1], 1);
   load_scale_part<0, 1>(c, chunks[1], 1);
@@ -379,6 +442,39 @@ __device__ __forceinline__ void set_tile(Ctx& c, int p, int tiles_m, int tiles_n
   tile_of(p, tiles_m, tiles_n, tm, tn);
   c.row0 = tm * kTileM;
   c.col0 = tn * kTileN;
+  // Wave's first code row, clamped like the rows of its loads: rows past M
+  // (or N) re-read the last 8 rows, computed but never stored.
+  const int ra = min(c.row0 + 64 * c.wave, c.M - 8);
+  const int rb = min(c.col0 + 64 * c.wave, c.N - 8);
+  c.tile_a = c.A + (int64_t)ra * c.row_bytes - kDmaBias;
+  c.tile_b = c.B + (int64_t)rb * c.row_bytes - kDmaBias;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int ga = min(c.row0 + 64 * c.wave + 8 * q, c.M - 8) - ra;
+    const int gb = min(c.col0 + 64 * c.wave + 8 * q, c.N - 8) - rb;
+    c.off_a[q] = (uint32_t)(ga * c.row_bytes) + c.code_lane[q & 1] + kDmaBias - (q % 4) * 1024;
+    c.off_b[q] = (uint32_t)(gb * c.row_bytes) + c.code_lane[q & 1] + kDmaBias - (q % 4) * 1024;
+  }
+  // Scale pairs: part U = 2p + e of operand X reads row
+  // origin + 128 (U / 4) + 8 (U % 4) + 2 w + scale_lane (clamped), half-step
+  // scale_t ^ (4 e + w); offsets relative to part 2p's clamped first row.
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    const int origin = x == 0 ? c.row0 : c.col0;
+    const int rows = x == 0 ? c.M : c.N;
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp) {
+      const int row_u = origin + 128 * (pp / 2) + 16 * (pp % 2) + 2 * c.wave;
+      const int row_c = min(row_u, rows - 1);
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int lane_row = min(row_u + 8 * e + c.scale_lane, rows - 1) - row_c;
+        const int t = c.scale_t ^ (4 * e + c.wave);
+        c.soff[x][pp][e] =
+            (uint32_t)(lane_row * c.scale_row_bytes + 4 * t + kScaleBias - 1024 * e);
+      }
+    }
+  }
 }
 
 // FP32 (or BF16) epilogue straight from the accumulators.
@@ -461,12 +557,12 @@ __device__ __forceinline__ void store_tile_bf16_lds(const Ctx& c, v16f_t (&acc)[
   }
 }
 
-template <bool kOutFp32>
+template <bool kOutFp32, bool kFull>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_tile_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ As,
                       const uint8_t* __restrict__ B, const uint8_t* __restrict__ Bs, int M, int N,
                       int K, void* __restrict__ C, int tiles_m, int tiles_n) {
-  __shared__ Slot slot0, slot1;
+  __shared__ Tiles tl;
   __shared__ __align__(16) uint8_t chunks[2][2 * kChunkBytes];
 
   const int tid = threadIdx.x;
@@ -502,6 +598,11 @@ void gemm_tile_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__
   c.a_base = (wy * 128 + r) * kRowBytes;
   c.b_base = (wx * 128 + r) * kRowBytes;
   c.frag_x = (uint32_t)((h ^ chunk_swizzle(r)) << 4);
+#pragma unroll
+  for (int sl = 0; sl < 4; ++sl) {
+    c.fa_off[sl] = (uint32_t)c.a_base + ((uint32_t)(32 * sl) ^ c.frag_x);
+    c.fb_off[sl] = (uint32_t)c.b_base + ((uint32_t)(32 * sl) ^ c.frag_x);
+  }
   c.s_off = 16 * kChunk * (wy * 32 + r);
   c.sb_off = 16 * kChunk * (wx * 32 + r);
   c.s_x = (r >> 1) & 7;
@@ -512,8 +613,8 @@ void gemm_tile_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__
   // grid is a multiple of 8, so every tile id keeps its workgroup's XCD.
   int p = blockIdx.x;
   set_tile(c, p, tiles_m, tiles_n);
-  issue_tile_head(c, slot0, chunks);
-  issue_tile_tail(c, slot1, chunks);
+  issue_tile_head(c, tl, chunks);
+  issue_tile_tail(c, tl, chunks);
   for (; p < total; p += gridDim.x) {
     asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
 
@@ -525,22 +626,22 @@ void gemm_tile_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__
     Frags fa, fb;
     HalfScales sc0, sc1;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) read_frag_b(c, slot0, 0, j, fa.b[j]);
+    for (int j = 0; j < 4; ++j) read_frag_b<0>(c, tl, 0, j, fa.b[j]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) read_frag_a(c, slot0, 0, i, fa.a[i]);
+    for (int i = 0; i < 4; ++i) read_frag_a<0>(c, tl, 0, i, fa.a[i]);
     read_half_scales(c, chunks[0], 0, sc0);
     read_half_scales(c, chunks[0], 1, sc1);
 
     int T = 0;
     for (; T + 4 <= ksteps; T += 4) {
-      k_step<1>(c, slot0, slot1, chunks, acc, fa, fb, sc0, sc1, T);
-      k_step<2>(c, slot1, slot0, chunks, acc, fa, fb, sc0, sc1, T + 1);
-      k_step<3>(c, slot0, slot1, chunks, acc, fa, fb, sc0, sc1, T + 2);
-      k_step<0>(c, slot1, slot0, chunks, acc, fa, fb, sc0, sc1, T + 3);
+      k_step<kFull, 1, 0>(c, tl, chunks, acc, fa, fb, sc0, sc1, T);
+      k_step<kFull, 2, 1>(c, tl, chunks, acc, fa, fb, sc0, sc1, T + 1);
+      k_step<kFull, 3, 0>(c, tl, chunks, acc, fa, fb, sc0, sc1, T + 2);
+      k_step<kFull, 0, 1>(c, tl, chunks, acc, fa, fb, sc0, sc1, T + 3);
     }
-    if (T < ksteps) k_step<1>(c, slot0, slot1, chunks, acc, fa, fb, sc0, sc1, T);
-    if (T + 1 < ksteps) k_step<2>(c, slot1, slot0, chunks, acc, fa, fb, sc0, sc1, T + 1);
-    if (T + 2 < ksteps) k_step<3>(c, slot0, slot1, chunks, acc, fa, fb, sc0, sc1, T + 2);
+    if (T < ksteps) k_step<kFull, 1, 0>(c, tl, chunks, acc, fa, fb, sc0, sc1, T);
+    if (T + 1 < ksteps) k_step<kFull, 2, 1>(c, tl, chunks, acc, fa, fb, sc0, sc1, T + 1);
+    if (T + 2 < ksteps) k_step<kFull, 3, 0>(c, tl, chunks, acc, fa, fb, sc0, sc1, T + 2);
     // Every load of this tile has landed and every LDS read has returned,
     // in all waves, before the next tile's loads reuse the buffers.
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -552,21 +653,22 @@ void gemm_tile_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__
       const Ctx cur_tile = c;
       if (pn < total) {
         set_tile(c, pn, tiles_m, tiles_n);
-        issue_tile_head(c, slot0, chunks);
+        issue_tile_head(c, tl, chunks);
       }
       store_tile<kOutFp32>(cur_tile, acc, wy, wx, r, h, C);
     } else {
-      // Waves 0, 1 park their blocks in slot0, waves 2, 3 in slot1; the next
-      // tile's loads wait until every wave has read its block back.
-      uint8_t* region = (wave < 2 ? slot0.a : slot1.a) + (wave & 1) * 32768;
+      // Waves 0, 1 park their blocks in the A slots, waves 2, 3 in the B
+      // slots; the next tile's loads wait until every wave has read its
+      // block back.
+      uint8_t* region = wave < 2 ? tl.a[wave] : tl.b[wave - 2];
       store_tile_bf16_lds(c, acc, wy, wx, lane, region, C);
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
       if (pn < total) {
         set_tile(c, pn, tiles_m, tiles_n);
-        issue_tile_head(c, slot0, chunks);
+        issue_tile_head(c, tl, chunks);
       }
     }
-    if (pn < total) issue_tile_tail(c, slot1, chunks);
+    if (pn < total) issue_tile_tail(c, tl, chunks);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
@@ -609,12 +711,19 @@ hipError_t launch_gemm(const void* A, const void* As, const void* B, const void*
   const auto* as = static_cast<const uint8_t*>(As);
   const auto* b = static_cast<const uint8_t*>(B);
   const auto* bs = static_cast<const uint8_t*>(Bs);
-  if (out_fp32)
-    hipLaunchKernelGGL(gemm_tile_kernel<true>, grid, dim3(kThreads), 0, stream, a, as, b, bs, M, N,
-                       K, C, tiles_m, tiles_n);
+  const bool full = K % 1024 == 0;
+  if (out_fp32 && full)
+    hipLaunchKernelGGL((gemm_tile_kernel<true, true>), grid, dim3(kThreads), 0, stream, a, as, b,
+                       bs, M, N, K, C, tiles_m, tiles_n);
+  else if (out_fp32)
+    hipLaunchKernelGGL((gemm_tile_kernel<true, false>), grid, dim3(kThreads), 0, stream, a, as, b,
+                       bs, M, N, K, C, tiles_m, tiles_n);
+  else if (full)
+    hipLaunchKernelGGL((gemm_tile_kernel<false, true>), grid, dim3(kThreads), 0, stream, a, as, b,
+                       bs, M, N, K, C, tiles_m, tiles_n);
   else
-    hipLaunchKernelGGL(gemm_tile_kernel<false>, grid, dim3(kThreads), 0, stream, a, as, b, bs, M,
-                       N, K, C, tiles_m, tiles_n);
+    hipLaunchKernelGGL((gemm_tile_kernel<false, false>), grid, dim3(kThreads), 0, stream, a, as, b,
+                       bs, M, N, K, C, tiles_m, tiles_n);
   return hipGetLastError();
 }
 
