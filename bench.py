@@ -197,6 +197,31 @@ def main():
     q_bytes = M * K * 2 + M * K // 2 + M * K // 32
     quant_gbps = q_bytes / (q_ms.mean() * 1e-3) / 1e9
 
+    # Bidimensional quantize (rowwise + columnwise outputs) of the same
+    # activation, timed alone: a widening of the quantize step.
+    q2_out = (torch.empty((M, K // 2), dtype=torch.uint8, device=dev),
+              torch.empty((M, K // 32), dtype=torch.uint8, device=dev),
+              torch.empty((K, M // 2), dtype=torch.uint8, device=dev),
+              torch.empty((K, M // 32), dtype=torch.uint8, device=dev))
+    q2_ms = None
+    if M % 32 == 0:
+        def q2():
+            rc = mx.mxfp4_quantize_2d(x.data_ptr(), M, K, *(t.data_ptr() for t in q2_out),
+                                      stream.cuda_stream)
+            if rc != 0:
+                raise mx.Mxfp4Error(rc, "mxfp4_quantize_2d")
+        for _ in range(3):
+            q2()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(20):
+            q2()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        q2_ms = e0.elapsed_time(e1) / 20
+    q2_bytes = 2 * M * K + 2 * (M * K // 2 + M * K // 32)
+
     traffic = read_traffic(args.traffic_json, w.name)
     out_bytes = 4 if w.out_dtype == mx.OUT_FP32 else 2
     gemm_bytes = (M + N) * (K // 2 + K // 32) + M * N * out_bytes
@@ -234,6 +259,8 @@ def main():
         "quantize_gbps": quant_gbps,
         "quantize_ms": float(q_ms.mean()),
         "quantize_hbm_frac": quant_gbps / HBM_PEAK_GBPS,
+        "quantize_2d_ms": q2_ms,
+        "quantize_2d_gbps": None if q2_ms is None else q2_bytes / (q2_ms * 1e-3) / 1e9,
         "wall_s_timed": t_wall,
         "gemm_gbps_algorithmic": gemm_gbps,
         "b_copies_rotated": copies,

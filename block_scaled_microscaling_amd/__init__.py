@@ -6,8 +6,9 @@ marshals arguments. PyTorch supplies device memory and streams.
 
 Two layers, same names as the C ABI:
   * mxfp4_available, mxfp4_strerror, mxfp4_quantize, mxfp4_quantize_async,
-    mxfp4_gemm take raw device pointers (ints) and return the C status code.
-  * quantize(x) and gemm(...) take torch tensors, check their dtype, device,
+    mxfp4_quantize_2d, mxfp4_gemm take raw device pointers (ints) and return
+    the C status code.
+  * quantize(x), quantize_2d(x) and gemm(...) take torch tensors, check their dtype, device,
     shape and contiguity, allocate outputs when none are given, enqueue on
     torch's current stream and raise Mxfp4Error on a non-zero status.
 
@@ -20,7 +21,7 @@ import os
 __all__ = [
     "Mxfp4Error", "OUT_BF16", "OUT_FP32", "library_path", "load_library",
     "mxfp4_available", "mxfp4_strerror", "mxfp4_quantize", "mxfp4_quantize_async",
-    "mxfp4_gemm", "quantize", "gemm",
+    "mxfp4_quantize_2d", "mxfp4_gemm", "quantize", "quantize_2d", "gemm",
 ]
 
 OUT_BF16 = 0
@@ -55,6 +56,8 @@ def load_library():
         lib.mxfp4_quantize.restype = i32
         lib.mxfp4_quantize_async.argtypes = [vp, i64, i64, vp, vp, vp]
         lib.mxfp4_quantize_async.restype = i32
+        lib.mxfp4_quantize_2d.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp]
+        lib.mxfp4_quantize_2d.restype = i32
         lib.mxfp4_gemm.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, vp, vp]
         lib.mxfp4_gemm.restype = i32
         _lib = lib
@@ -76,6 +79,11 @@ def mxfp4_quantize(x_bf16, M, K, codes_out, scales_out):
 
 def mxfp4_quantize_async(x_bf16, M, K, codes_out, scales_out, stream):
     return int(load_library().mxfp4_quantize_async(x_bf16, M, K, codes_out, scales_out, stream))
+
+
+def mxfp4_quantize_2d(x_bf16, M, K, codes_row, scales_row, codes_col, scales_col, stream):
+    return int(load_library().mxfp4_quantize_2d(x_bf16, M, K, codes_row, scales_row, codes_col,
+                                                scales_col, stream))
 
 
 def mxfp4_gemm(A_codes, A_scales, B_codes, B_scales, M, N, K, out_dtype, C, stream):
@@ -125,6 +133,29 @@ def quantize(x, codes=None, scales=None, stream=None):
     if rc != 0:
         raise Mxfp4Error(rc, "mxfp4_quantize")
     return codes, scales
+
+
+def quantize_2d(x, stream=None):
+    """Row-wise and column-wise BF16 -> MXFP4 in one pass. x: bfloat16 [M, K].
+
+    Returns (codes [M, K/2], scales [M, K/32], codes_t [K, M/2], scales_t
+    [K, M/32]), uint8: the MXFP4 forms of x and of x^T.
+    """
+    import torch
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [M, K]")
+    M, K = x.shape
+    _check(x, "x", torch.bfloat16, (M, K))
+    dev = x.device
+    codes = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((M, K // 32), dtype=torch.uint8, device=dev)
+    codes_t = torch.empty((K, M // 2), dtype=torch.uint8, device=dev)
+    scales_t = torch.empty((K, M // 32), dtype=torch.uint8, device=dev)
+    rc = mxfp4_quantize_2d(x.data_ptr(), M, K, codes.data_ptr(), scales.data_ptr(),
+                           codes_t.data_ptr(), scales_t.data_ptr(), _stream_handle(stream))
+    if rc != 0:
+        raise Mxfp4Error(rc, "mxfp4_quantize_2d")
+    return codes, scales, codes_t, scales_t
 
 
 def gemm(A_codes, A_scales, B_codes, B_scales, out_dtype=None, out=None, stream=None):

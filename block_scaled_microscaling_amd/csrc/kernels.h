@@ -12,6 +12,11 @@ namespace mxfp4 {
 hipError_t launch_quantize(const void* x_bf16, int64_t nblocks, void* codes, void* scales,
                            hipStream_t stream);
 
+// Row-wise and column-wise MXFP4 of X [M, K] in one pass: codes_row [M, K/2],
+// scales_row [M, K/32], codes_col [K, M/2], scales_col [K, M/32].
+hipError_t launch_quantize_2d(const void* x_bf16, int M, int K, void* codes_row, void* scales_row,
+                              void* codes_col, void* scales_col, hipStream_t stream);
+
 // C[M,N] = A[M,K] * B[N,K]^T with block scales; out_fp32 selects FP32 vs BF16.
 hipError_t launch_gemm(const void* A, const void* As, const void* B, const void* Bs, int M,
                        int N, int K, bool out_fp32, void* C, hipStream_t stream);

@@ -67,6 +67,23 @@ int mxfp4_quantize(const void* x_bf16, int64_t M, int64_t K, void* codes_out,
 int mxfp4_quantize_async(const void* x_bf16, int64_t M, int64_t K, void* codes_out,
                          void* scales_out, void* stream);
 
+/* Bidimensional quantize: one pass over X [M, K] writes the row-wise MXFP4
+ * form (exactly what mxfp4_quantize writes) and the row-wise MXFP4 form of
+ * X^T, i.e. blocks of 32 consecutive rows of each column, the operand of a
+ * GEMM that contracts over M (the weight gradient of a linear layer). It is
+ * the rowwise + columnwise ("bidimensional") quantize of the NVFP4 kernels
+ * on NVIDIA/TransformerEngine #3809 (description), for MXFP4 blocks.
+ * x_bf16 [M, K] row-major BF16, 16-byte aligned
+ * codes_row [M, K/2], scales_row [M, K/32]: as mxfp4_quantize
+ * codes_col [K, M/2]: byte i of row k packs X[2i][k] (low nibble) and
+ *   X[2i+1][k]; scales_col [K, M/32]: scale of rows 32j..32j+31 of column k
+ * codes_row, codes_col 16-byte aligned; scales byte-addressed
+ * Requires M, K >= 32, M % 32 == 0, K % 32 == 0, M * K < 2^40; otherwise
+ * MXFP4_EINVAL (MXFP4_EALIGN for alignment) and nothing is launched.
+ * Asynchronous on `stream` (a hipStream_t, or NULL for the null stream). */
+int mxfp4_quantize_2d(const void* x_bf16, int64_t M, int64_t K, void* codes_row,
+                      void* scales_row, void* codes_col, void* scales_col, void* stream);
+
 /* Block-scaled GEMM, TN: C[m, n] = sum_k dq(A[m, k]) * dq(B[n, k]) with
  * dq(code, scale) = E2M1(code) * 2^(scale - 127), fp32 accumulation; the
  * capability gates of the hipBLASLt MXFP4 path on "Integrate MXFP4 hipblaslt

@@ -13,6 +13,7 @@ from .mxfp4_ref import (  # noqa: F401
     scale_exponent,
     e2m1_nearest_even,
     quantize,
+    quantize_2d,
     unpack_codes,
     dequantize,
     gemm,

@@ -17,6 +17,9 @@ Sources, by page title and section:
   * "feat(ck-tile): aquant GEMM TE to dispatcher bridge" (ROCm/rocm-libraries
     #9980), pk_int4 heap-overflow fix: packed 4-bit data holds two values per
     byte.
+  * NVIDIA/TransformerEngine #3809, description: a bidimensional quantize
+    writes both the rowwise and the columnwise (transposed) quantized forms
+    of one input (quantize_2d below).
 
 The pages never state the numbers of the format. Readings taken here, the
 plainest ones consistent with the pages:
@@ -109,6 +112,20 @@ def quantize(x_bits):
         code = code.reshape(r1 - r0, K)
         codes[r0:r1] = code[:, 0::2] | (code[:, 1::2] << 4)  # R4
     return codes, scales
+
+
+def quantize_2d(x_bits):
+    """Rowwise and columnwise MXFP4 of X [M, K] (BF16 bits): the rowwise form
+    of X and the rowwise form of X^T, i.e. blocks of 32 consecutive rows of
+    each column (R2-R5 applied to X^T). M and K must be multiples of 32.
+
+    Returns (codes [M, K/2], scales [M, K/32], codes_t [K, M/2], scales_t
+    [K, M/32]).
+    """
+    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    codes, scales = quantize(x_bits)
+    codes_t, scales_t = quantize(np.ascontiguousarray(x_bits.T))
+    return codes, scales, codes_t, scales_t
 
 
 def unpack_codes(codes):

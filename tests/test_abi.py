@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
     lib = mx.load_library()
     names = _declared_functions()
     assert names == ["mxfp4_available", "mxfp4_gemm", "mxfp4_quantize",
-                     "mxfp4_quantize_async", "mxfp4_strerror"]
+                     "mxfp4_quantize_2d", "mxfp4_quantize_async", "mxfp4_strerror"]
     for n in names:
         assert hasattr(lib, n), n
 
@@ -94,12 +94,31 @@ def test_quantize_rejects_nulls_and_misalignment():
     assert mx.mxfp4_quantize(P16, 4, 32, P16 + 2, P16) == EALIGN
 
 
+@pytest.mark.parametrize("M,K", [(0, 32), (32, 0), (16, 32), (32, 16), (48, 64), (64, 48),
+                                 (1 << 31, 32), (1 << 20, 1 << 20)])
+def test_quantize_2d_rejects_bad_sizes(M, K):
+    assert mx.mxfp4_quantize_2d(P16, M, K, P16, P16, P16, P16, None) == EINVAL
+
+
+def test_quantize_2d_rejects_nulls_and_misalignment():
+    args = [P16, 64, 64, P16, P16, P16, P16, None]
+    for i in (0, 3, 4, 5, 6):
+        bad = list(args)
+        bad[i] = None
+        assert mx.mxfp4_quantize_2d(*bad) == EINVAL
+    for i in (0, 3, 5):
+        bad = list(args)
+        bad[i] = P16 + 8
+        assert mx.mxfp4_quantize_2d(*bad) == EALIGN
+
+
 def test_no_device_reports_unsupported():
     """Valid arguments with no gfx950 device current: rc -2, nothing launched."""
     if mx.mxfp4_available() != 0:
         pytest.skip("a gfx950 device is present; stand-in pointers must not reach it")
     assert mx.mxfp4_gemm(P16, P16, P16, P16, 32, 32, 256, mx.OUT_BF16, P16, None) == EUNSUPPORTED
     assert mx.mxfp4_quantize(P16, 4, 32, P16, P16) == EUNSUPPORTED
+    assert mx.mxfp4_quantize_2d(P16, 32, 32, P16, P16, P16, P16, None) == EUNSUPPORTED
 
 
 def test_tensor_layer_validates_before_calling():

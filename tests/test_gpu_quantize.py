@@ -154,3 +154,63 @@ def test_side_stream_and_null_stream_entry():
     assert mx.mxfp4_quantize(x.data_ptr(), 64, 512, c2.data_ptr(), s2.data_ptr()) == 0
     torch.cuda.synchronize()
     assert np.array_equal(c2.cpu().numpy(), rc) and np.array_equal(s2.cpu().numpy(), rs)
+
+
+# ------------------------------------------------- bidimensional quantize
+# Rowwise + columnwise MXFP4 in one pass (the bidimensional quantize of
+# NVIDIA/TransformerEngine #3809, description): both outputs bit-exact with
+# the oracle's quantize of X and of X^T.
+def _assert_same_2d(bits):
+    x = bf16_to_dev(bits)
+    gc, gs, gct, gst = (t.cpu().numpy() for t in mx.quantize_2d(x))
+    torch.cuda.synchronize()
+    rc, rs, rct, rst = oracle.quantize_2d(bits)
+    for name, g, r in (("codes", gc, rc), ("scales", gs, rs), ("codes_t", gct, rct),
+                       ("scales_t", gst, rst)):
+        bad = np.argwhere(g != r)
+        assert bad.size == 0, f"{name}: {bad.shape[0]} bytes differ, first {bad[:4].tolist()}"
+
+
+@pytest.mark.parametrize("M,K", [(32, 32), (128, 128), (256, 384), (160, 96), (4128, 7936),
+                                 (96, 4128), (1056, 352)])
+def test_quantize_2d_random(M, K):
+    """Random finite bit patterns; shapes with whole and ragged 128 x 128 tiles."""
+    announce(f"quantize_2d random {M}x{K}")
+    _assert_same_2d(random_bf16_bits((M, K), seed=M * 7 + K))
+
+
+def test_quantize_2d_every_bf16_value():
+    """All finite BF16 values as columns' elements: 65280 columns of 32 rows,
+    each holding the value at row 5 and its negation at row 30 in a column of
+    a fixed partner value (the exhaustive rowwise test, transposed), plus the
+    same values along rows."""
+    announce("quantize_2d exhaustive")
+    xs = np.arange(0, 1 << 16, dtype=np.uint32).astype(np.uint16)
+    xs = xs[(xs & 0x7F80) != 0x7F80][:65280]
+    cols = np.full((32, xs.size), 0x40c0, dtype=np.uint16)
+    cols[5] = xs
+    cols[30] = xs ^ np.uint16(0x8000)
+    _assert_same_2d(cols)
+
+
+@pytest.mark.parametrize("name", ["ragged", "square"])
+def test_quantize_2d_workload(name):
+    """The workload's activation at full size; the square one is compared on
+    sampled rows of both outputs (the oracle quantizes those rows itself)."""
+    w = WORKLOADS[name]
+    announce(f"quantize_2d workload {name}: {w.M}x{w.K}")
+    bits = bf16_matrix((w.M, w.K), w.a_dist, w.a_seed)
+    if name == "ragged":
+        _assert_same_2d(bits)
+        return
+    gc, gs, gct, gst = mx.quantize_2d(bf16_to_dev(bits))
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(11)
+    rows = np.sort(rng.choice(w.M, 64, replace=False))
+    cols = np.sort(rng.choice(w.K, 64, replace=False))
+    rc, rs = oracle.quantize(bits[rows])
+    assert np.array_equal(gc.cpu().numpy()[rows], rc)
+    assert np.array_equal(gs.cpu().numpy()[rows], rs)
+    rct, rst = oracle.quantize(np.ascontiguousarray(bits[:, cols].T))
+    assert np.array_equal(gct.cpu().numpy()[cols], rct)
+    assert np.array_equal(gst.cpu().numpy()[cols], rst)

@@ -131,6 +131,33 @@ def test_q2_hand_worked():
     assert oracle.unpack_codes(codes)[0].tolist() == [int(v, 16) for v in g["codes"]]
 
 
+def test_quantize_2d_columns_hand_worked():
+    """Columnwise form (NVIDIA/TransformerEngine #3809, bidimensional quantize):
+    a 32 x 64 X whose column 5 is the hand-worked Q1 block (others zero) must
+    give Q1's packed codes and scale in row 5 of the transposed output, and
+    Q1-free rows elsewhere; the rowwise form is the plain quantize."""
+    g = read_golden("q1_block.txt")
+    x = np.zeros((32, 64), dtype=np.uint16)
+    x[:, 5] = _f2bits([float(v) for v in g["input"]])
+    codes, scales, codes_t, scales_t = oracle.quantize_2d(x)
+    assert codes_t.shape == (64, 16) and scales_t.shape == (64, 1)
+    assert codes_t[5].tolist() == [int(v, 16) for v in g["packed"]]
+    assert scales_t[5].tolist() == [int(g["scale"][0])]
+    others = np.delete(np.arange(64), 5)
+    assert np.all(codes_t[others] == 0) and np.all(scales_t[others] == 0)
+    rc, rs = oracle.quantize(x)
+    assert np.array_equal(codes, rc) and np.array_equal(scales, rs)
+
+
+def test_quantize_2d_transpose_symmetry():
+    """The columnwise outputs of X are the rowwise outputs of X^T and back."""
+    x = random_bf16_bits((64, 96), 12345)
+    c, s, ct, st = oracle.quantize_2d(x)
+    c2, s2, ct2, st2 = oracle.quantize_2d(np.ascontiguousarray(x.T))
+    assert np.array_equal(ct, c2) and np.array_equal(st, s2)
+    assert np.array_equal(c, ct2) and np.array_equal(s, st2)
+
+
 # --------------------------------------------------------------- invariants
 def test_sign_flip_invariant():
     bits = random_bf16_bits((16, 256), seed=11)
