@@ -4,23 +4,26 @@
 // X^T (blocks of 32 along M), as [K, M/2] codes and [K, M/32] scales.
 //
 // The column-wise operand is what a GEMM contracting over M needs (the
-// weight-gradient product of a linear layer). The single-pass design, row
-// blocks straight from registers and only the transposed direction staged
-// through on-chip memory, is the bidimensional quantize kernel described on
-// NVIDIA/TransformerEngine #3809 (description); the block arithmetic is the
-// one of quantize.hip (integer amax of |bits|, scale byte = max(E_field(amax)
-// - 2, 0), v_cvt_scalef32_pk_fp4_bf16 for RNE E2M1 codes).
+// weight-gradient product of a linear layer). The single-pass design (row
+// blocks encoded straight from registers, only the transposed direction
+// staged through on-chip memory) is the bidimensional quantize kernel
+// described on NVIDIA/TransformerEngine #3809 (description); the block
+// arithmetic is the one of quantize.hip (integer amax of |bits|, scale byte
+// = max(E_field(amax) - 2, 0), v_cvt_scalef32_pk_fp4_bf16 for RNE E2M1).
 //
-// Work mapping: a workgroup of 256 threads owns a 128 x 128 tile.
-//   Row phase: thread t takes row t / 2, columns 64 (t % 2) .. +63 (two MX
-//   blocks, eight 16-byte loads), encodes them from registers and parks the
-//   tile in LDS (rows padded to 272 bytes so the 16-byte writes of 8 rows
-//   fall on distinct banks).
-//   Column phase: thread t takes columns 2 (t % 64), +1 and rows
-//   32 (t / 64) .. +31: 32 dword reads (both columns at once), an integer
-//   amax per column, 16 byte-permutes per column to pair consecutive rows,
-//   and 16 conversions per column.
-// Edge tiles (M or K not a multiple of 128) mask whole 32-element blocks.
+// Work mapping: a workgroup of 256 threads owns a 256-row x 128-column tile.
+//   Row phase: load i of thread t reads the 16-byte chunk t % 16 of row
+//   16 i + t / 16: 16 lanes per 256-byte row segment, so each wave load
+//   fetches 4 rows x 2 whole lines; four consecutive lanes hold one MX block
+//   (amax finished with two quad DPP moves). The tile is parked in LDS with
+//   rows padded to 272 bytes.
+//   Column phase: thread t takes columns 2 (t % 64), +1 and row blocks
+//   2 (t / 64), +1: 32 dword reads per row block (both columns at once), an
+//   integer amax per column, byte permutes pairing consecutive rows, 16
+//   conversions per column block. The column codes and scales are parked in
+//   LDS again and written with 8 lanes per 128-byte column segment: whole
+//   cache lines per store.
+// Edge tiles (M or K not multiples of the tile) mask whole 32-element blocks.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -34,8 +37,9 @@ typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
-constexpr int kTile = 128;
-constexpr int kLdsRow = 2 * kTile + 16;  // bytes per LDS row (padded)
+constexpr int kRows = 256;
+constexpr int kCols = 128;
+constexpr int kLdsRow = 2 * kCols + 16;  // 272 bytes
 
 __device__ __forceinline__ u16x2_t abs_pair(uint32_t w) {
   return __builtin_bit_cast(u16x2_t, w & 0x7FFF7FFFu);
@@ -49,8 +53,6 @@ __device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t w) {
 __device__ __forceinline__ uint32_t scale_byte(uint32_t amax_bits) {
   return (uint32_t)max((int)(amax_bits >> 7) - 2, 0);
 }
-// Four BF16 pairs (8 elements, element 2i in the low half of word i) to 8
-// E2M1 codes, element 2i in the low nibble of byte i.
 __device__ __forceinline__ uint32_t encode8(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3,
                                             float scale) {
   uint32_t r = 0;
@@ -60,65 +62,65 @@ __device__ __forceinline__ uint32_t encode8(uint32_t w0, uint32_t w1, uint32_t w
   r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, as_bf16x2(w3), scale, 3);
   return r;
 }
+__device__ __forceinline__ uint32_t quad_max(uint32_t v) {
+  uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);
+  v = max(v, o);
+  o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);
+  return max(v, o);
+}
 
 __global__ __launch_bounds__(kThreads) void quantize_2d_kernel(
     const uint8_t* __restrict__ x, int M, int K, uint8_t* __restrict__ codes_row,
     uint8_t* __restrict__ scales_row, uint8_t* __restrict__ codes_col,
     uint8_t* __restrict__ scales_col) {
-  __shared__ __align__(16) uint8_t tile[kTile * kLdsRow];
+  __shared__ __align__(16) uint8_t tile[kRows * kLdsRow];
   const int t = threadIdx.x;
-  const int m0 = blockIdx.y * kTile;
-  const int c0 = blockIdx.x * kTile;
+  const int m0 = blockIdx.y * kRows;
+  const int c0 = blockIdx.x * kCols;
   const int64_t row_bytes = 2 * (int64_t)K;
 
-  // Row phase.
+  // Row phase: load i covers rows 16 i + t / 16, 16-byte chunk t % 16.
   {
-    const int r = t >> 1;
-    const int half = t & 1;
-    const int m = m0 + r;
-    const int cb = c0 + 64 * half;  // first column of this thread's two blocks
-    u32x4_t v[8];
+    const int chunk = t & 15;
+    const int col = c0 + 8 * chunk;
+    u32x4_t v[16];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int col = cb + 8 * i;
+    for (int i = 0; i < 16; ++i) {
+      const int m = m0 + 16 * i + (t >> 4);
       v[i] = (m < M && col < K)
                  ? __builtin_nontemporal_load(
                        reinterpret_cast<const u32x4_t*>(x + m * row_bytes + 2 * (int64_t)col))
                  : u32x4_t{0u, 0u, 0u, 0u};
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      *reinterpret_cast<u32x4_t*>(tile + r * kLdsRow + 128 * half + 16 * i) = v[i];
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const int col = cb + 32 * b;
-      u16x2_t mx = abs_pair(v[4 * b][0]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) mx = max2(mx, abs_pair(v[4 * b + i][j]));
-      const uint32_t byte = scale_byte(max((uint32_t)mx.x, (uint32_t)mx.y));
-      const float scale = __uint_as_float(byte << 23);
-      u32x4_t out;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const u32x4_t q = v[4 * b + i];
-        out[i] = encode8(q[0], q[1], q[2], q[3], scale);
-      }
+    for (int i = 0; i < 16; ++i) {
+      const int r = 16 * i + (t >> 4);
+      *reinterpret_cast<u32x4_t*>(tile + r * kLdsRow + 16 * chunk) = v[i];
+      const u32x4_t q = v[i];
+      const u16x2_t mx = max2(max2(abs_pair(q[0]), abs_pair(q[1])),
+                              max2(abs_pair(q[2]), abs_pair(q[3])));
+      const uint32_t amax = quad_max(max((uint32_t)mx.x, (uint32_t)mx.y));
+      const uint32_t byte = scale_byte(amax);
+      const uint32_t c = encode8(q[0], q[1], q[2], q[3], __uint_as_float(byte << 23));
+      const int m = m0 + r;
       if (m < M && col < K) {
-        *reinterpret_cast<u32x4_t*>(codes_row + (int64_t)m * (K / 2) + col / 2) = out;
-        scales_row[(int64_t)m * (K / 32) + col / 32] = (uint8_t)byte;
+        *reinterpret_cast<uint32_t*>(codes_row + (int64_t)m * (K / 2) + col / 2) = c;
+        if ((t & 3) == 0) scales_row[(int64_t)m * (K / 32) + col / 32] = (uint8_t)byte;
       }
     }
   }
   __syncthreads();
 
-  // Column phase: columns k0 = c0 + 2 cp and k0 + 1, rows mb .. mb + 31.
-  {
-    const int cp = t & 63;
-    const int rb = t >> 6;
-    const int k0 = c0 + 2 * cp;
-    const int mb = m0 + 32 * rb;
+  // Column phase: columns c0 + 2 cp, +1; row blocks 2 bp, 2 bp + 1. The
+  // codes and scales are parked in LDS (the tile is dead by then) and written
+  // out with whole lines: 8 lanes per 128-byte column segment.
+  const int cp = t & 63;
+  const int bp = t >> 6;
+  u32x4_t out[2][2];
+  uint32_t sbyte[2][2];
+#pragma unroll
+  for (int rbi = 0; rbi < 2; ++rbi) {
+    const int rb = 2 * bp + rbi;
     uint32_t w[32];
 #pragma unroll
     for (int i = 0; i < 32; ++i)
@@ -130,9 +132,7 @@ __global__ __launch_bounds__(kThreads) void quantize_2d_kernel(
     for (int e = 0; e < 2; ++e) {
       const uint32_t byte = scale_byte(e == 0 ? (uint32_t)mx.x : (uint32_t)mx.y);
       const float scale = __uint_as_float(byte << 23);
-      // Pair rows 2i, 2i + 1 of column k0 + e: bytes (2e, 2e + 1) of each word.
       const uint32_t sel = e == 0 ? 0x05040100u : 0x07060302u;
-      u32x4_t out;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         uint32_t p[4];
@@ -141,12 +141,50 @@ __global__ __launch_bounds__(kThreads) void quantize_2d_kernel(
           const int i = 8 * g + 2 * j;
           p[j] = __builtin_amdgcn_perm(w[i + 1], w[i], sel);
         }
-        out[g] = encode8(p[0], p[1], p[2], p[3], scale);
+        out[rbi][e][g] = encode8(p[0], p[1], p[2], p[3], scale);
       }
-      const int k = k0 + e;
-      if (k < K && mb < M) {
-        *reinterpret_cast<u32x4_t*>(codes_col + (int64_t)k * (M / 2) + mb / 2) = out;
-        scales_col[(int64_t)k * (M / 32) + mb / 32] = (uint8_t)byte;
+      sbyte[rbi][e] = byte;
+    }
+  }
+  __syncthreads();
+  // Staging: column c's 128 code bytes at c * kColStage, its 8 scale bytes
+  // at kScaleStage + 8 c.
+  constexpr int kColStage = 144;
+  constexpr int kScaleStage = kCols * kColStage;
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int c = 2 * cp + e;
+#pragma unroll
+    for (int rbi = 0; rbi < 2; ++rbi) {
+      const int rb = 2 * bp + rbi;
+      *reinterpret_cast<u32x4_t*>(tile + c * kColStage + 16 * rb) = out[rbi][e];
+      tile[kScaleStage + 8 * c + rb] = (uint8_t)sbyte[rbi][e];
+    }
+  }
+  __syncthreads();
+  const int rows_valid = min(kRows, M - m0);  // multiple of 32
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int c = 32 * j + (t >> 3);
+    const int part = t & 7;  // 16-byte part = row block
+    const int k = c0 + c;
+    if (k < K && 32 * part < rows_valid)
+      *reinterpret_cast<u32x4_t*>(codes_col + (int64_t)k * (M / 2) + m0 / 2 + 16 * part) =
+          *reinterpret_cast<const u32x4_t*>(tile + c * kColStage + 16 * part);
+  }
+  if (t < kCols) {
+    const int k = c0 + t;
+    uint8_t* dst = scales_col + (int64_t)k * (M / 32) + m0 / 32;
+    if (k < K) {
+      // One 8-byte store when the destination is 8-byte aligned (base and
+      // row pitch) and the tile has all 8 row blocks.
+      if (rows_valid == kRows && (M / 32) % 8 == 0 &&
+          (reinterpret_cast<uintptr_t>(scales_col) & 7) == 0) {
+        *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(tile + kScaleStage + 8 * t);
+      } else {
+#pragma unroll
+        for (int rb = 0; rb < 8; ++rb)
+          if (32 * rb < rows_valid) dst[rb] = tile[kScaleStage + 8 * t + rb];
       }
     }
   }
@@ -156,7 +194,7 @@ __global__ __launch_bounds__(kThreads) void quantize_2d_kernel(
 
 hipError_t launch_quantize_2d(const void* x_bf16, int M, int K, void* codes_row, void* scales_row,
                               void* codes_col, void* scales_col, hipStream_t stream) {
-  const dim3 grid((K + kTile - 1) / kTile, (M + kTile - 1) / kTile);
+  const dim3 grid((K + kCols - 1) / kCols, (M + kRows - 1) / kRows);
   hipLaunchKernelGGL(quantize_2d_kernel, grid, dim3(kThreads), 0, stream,
                      static_cast<const uint8_t*>(x_bf16), M, K,
                      static_cast<uint8_t*>(codes_row), static_cast<uint8_t*>(scales_row),
