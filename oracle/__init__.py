@@ -20,6 +20,17 @@ from .mxfp4_ref import (  # noqa: F401
     gemm_block,
     gemm_entries,
 )
+from .stochastic import (  # noqa: F401
+    DIR_ROWWISE,
+    DIR_COLUMNWISE,
+    philox4x32,
+    seed_key,
+    sr_random_bytes,
+    sr_magnitude_index,
+    quantize_sr_with_bytes,
+    quantize_sr,
+    quantize_2d_sr,
+)
 from .compare import (  # noqa: F401
     FP32_REL_TOL,
     round_to_bf16,
