@@ -197,30 +197,46 @@ def main():
     q_bytes = M * K * 2 + M * K // 2 + M * K // 32
     quant_gbps = q_bytes / (q_ms.mean() * 1e-3) / 1e9
 
-    # Bidimensional quantize (rowwise + columnwise outputs) of the same
-    # activation, timed alone: a widening of the quantize step.
-    q2_out = (torch.empty((M, K // 2), dtype=torch.uint8, device=dev),
-              torch.empty((M, K // 32), dtype=torch.uint8, device=dev),
-              torch.empty((K, M // 2), dtype=torch.uint8, device=dev),
-              torch.empty((K, M // 32), dtype=torch.uint8, device=dev))
-    q2_ms = None
-    if M % 32 == 0:
-        def q2():
-            rc = mx.mxfp4_quantize_2d(x.data_ptr(), M, K, *(t.data_ptr() for t in q2_out),
-                                      stream.cuda_stream)
+    # Widenings of the quantize step, each timed alone on the same
+    # activation (20 back-to-back launches after 3 untimed ones): stochastic
+    # rounding, and the bidimensional (rowwise + columnwise) forms.
+    def time_alone(launch, name):
+        def once():
+            rc = launch()
             if rc != 0:
-                raise mx.Mxfp4Error(rc, "mxfp4_quantize_2d")
+                raise mx.Mxfp4Error(rc, name)
         for _ in range(3):
-            q2()
+            once()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for _ in range(20):
-            q2()
+            once()
         e1.record(stream)
         torch.cuda.synchronize()
-        q2_ms = e0.elapsed_time(e1) / 20
+        return e0.elapsed_time(e1) / 20
+
+    seed = 0x5EED
+    qsr_ms = time_alone(lambda: mx.mxfp4_quantize_sr(x.data_ptr(), M, K, seed, ac.data_ptr(),
+                                                     as_.data_ptr(), stream.cuda_stream),
+                        "mxfp4_quantize_sr")
+    q2_out = (torch.empty((M, K // 2), dtype=torch.uint8, device=dev),
+              torch.empty((M, K // 32), dtype=torch.uint8, device=dev),
+              torch.empty((K, M // 2), dtype=torch.uint8, device=dev),
+              torch.empty((K, M // 32), dtype=torch.uint8, device=dev))
+    q2_ms = q2sr_ms = None
+    if M % 32 == 0:
+        ptrs = [t.data_ptr() for t in q2_out]
+        q2_ms = time_alone(lambda: mx.mxfp4_quantize_2d(x.data_ptr(), M, K, *ptrs,
+                                                        stream.cuda_stream),
+                           "mxfp4_quantize_2d")
+        q2sr_ms = time_alone(lambda: mx.mxfp4_quantize_2d_sr(x.data_ptr(), M, K, seed, *ptrs,
+                                                             stream.cuda_stream),
+                             "mxfp4_quantize_2d_sr")
     q2_bytes = 2 * M * K + 2 * (M * K // 2 + M * K // 32)
+
+    def gbps(nbytes, ms):
+        return None if ms is None else nbytes / (ms * 1e-3) / 1e9
 
     traffic = read_traffic(args.traffic_json, w.name)
     out_bytes = 4 if w.out_dtype == mx.OUT_FP32 else 2
@@ -259,8 +275,12 @@ def main():
         "quantize_gbps": quant_gbps,
         "quantize_ms": float(q_ms.mean()),
         "quantize_hbm_frac": quant_gbps / HBM_PEAK_GBPS,
+        "quantize_sr_ms": qsr_ms,
+        "quantize_sr_gbps": gbps(q_bytes, qsr_ms),
         "quantize_2d_ms": q2_ms,
-        "quantize_2d_gbps": None if q2_ms is None else q2_bytes / (q2_ms * 1e-3) / 1e9,
+        "quantize_2d_gbps": gbps(q2_bytes, q2_ms),
+        "quantize_2d_sr_ms": q2sr_ms,
+        "quantize_2d_sr_gbps": gbps(q2_bytes, q2sr_ms),
         "wall_s_timed": t_wall,
         "gemm_gbps_algorithmic": gemm_gbps,
         "b_copies_rotated": copies,

@@ -6,9 +6,10 @@ marshals arguments. PyTorch supplies device memory and streams.
 
 Two layers, same names as the C ABI:
   * mxfp4_available, mxfp4_strerror, mxfp4_quantize, mxfp4_quantize_async,
-    mxfp4_quantize_2d, mxfp4_gemm take raw device pointers (ints) and return
-    the C status code.
-  * quantize(x), quantize_2d(x) and gemm(...) take torch tensors, check their dtype, device,
+    mxfp4_quantize_2d, mxfp4_quantize_sr, mxfp4_quantize_2d_sr, mxfp4_gemm
+    take raw device pointers (ints) and return the C status code.
+  * quantize(x), quantize_2d(x), quantize_sr(x, seed), quantize_2d_sr(x,
+    seed) and gemm(...) take torch tensors, check their dtype, device,
     shape and contiguity, allocate outputs when none are given, enqueue on
     torch's current stream and raise Mxfp4Error on a non-zero status.
 
@@ -21,7 +22,8 @@ import os
 __all__ = [
     "Mxfp4Error", "OUT_BF16", "OUT_FP32", "library_path", "load_library",
     "mxfp4_available", "mxfp4_strerror", "mxfp4_quantize", "mxfp4_quantize_async",
-    "mxfp4_quantize_2d", "mxfp4_gemm", "quantize", "quantize_2d", "gemm",
+    "mxfp4_quantize_2d", "mxfp4_quantize_sr", "mxfp4_quantize_2d_sr", "mxfp4_gemm",
+    "quantize", "quantize_2d", "quantize_sr", "quantize_2d_sr", "gemm",
 ]
 
 OUT_BF16 = 0
@@ -47,7 +49,7 @@ def load_library():
                 f"{library_path} is missing: build it with "
                 "`python -m block_scaled_microscaling_amd.build`")
         lib = ctypes.CDLL(library_path)
-        vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        vp, i64, i32, u64 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_uint64
         lib.mxfp4_available.argtypes = []
         lib.mxfp4_available.restype = i32
         lib.mxfp4_strerror.argtypes = [i32]
@@ -58,6 +60,10 @@ def load_library():
         lib.mxfp4_quantize_async.restype = i32
         lib.mxfp4_quantize_2d.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp]
         lib.mxfp4_quantize_2d.restype = i32
+        lib.mxfp4_quantize_sr.argtypes = [vp, i64, i64, u64, vp, vp, vp]
+        lib.mxfp4_quantize_sr.restype = i32
+        lib.mxfp4_quantize_2d_sr.argtypes = [vp, i64, i64, u64, vp, vp, vp, vp, vp]
+        lib.mxfp4_quantize_2d_sr.restype = i32
         lib.mxfp4_gemm.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, vp, vp]
         lib.mxfp4_gemm.restype = i32
         _lib = lib
@@ -84,6 +90,17 @@ def mxfp4_quantize_async(x_bf16, M, K, codes_out, scales_out, stream):
 def mxfp4_quantize_2d(x_bf16, M, K, codes_row, scales_row, codes_col, scales_col, stream):
     return int(load_library().mxfp4_quantize_2d(x_bf16, M, K, codes_row, scales_row, codes_col,
                                                 scales_col, stream))
+
+
+def mxfp4_quantize_sr(x_bf16, M, K, seed, codes_out, scales_out, stream):
+    return int(load_library().mxfp4_quantize_sr(x_bf16, M, K, seed, codes_out, scales_out,
+                                                stream))
+
+
+def mxfp4_quantize_2d_sr(x_bf16, M, K, seed, codes_row, scales_row, codes_col, scales_col,
+                         stream):
+    return int(load_library().mxfp4_quantize_2d_sr(x_bf16, M, K, seed, codes_row, scales_row,
+                                                   codes_col, scales_col, stream))
 
 
 def mxfp4_gemm(A_codes, A_scales, B_codes, B_scales, M, N, K, out_dtype, C, stream):
@@ -155,6 +172,61 @@ def quantize_2d(x, stream=None):
                            codes_t.data_ptr(), scales_t.data_ptr(), _stream_handle(stream))
     if rc != 0:
         raise Mxfp4Error(rc, "mxfp4_quantize_2d")
+    return codes, scales, codes_t, scales_t
+
+
+def _seed(seed):
+    seed = int(seed)
+    if not 0 <= seed < (1 << 64):
+        raise ValueError("seed must be in [0, 2**64)")
+    return seed
+
+
+def quantize_sr(x, seed, codes=None, scales=None, stream=None):
+    """Row-wise BF16 -> MXFP4 with stochastic rounding (Philox4x32-10 keyed by
+    block coordinates and the 64-bit `seed`). x: bfloat16 [M, K] on the GPU.
+
+    Returns (codes uint8 [M, K/2], scales uint8 [M, K/32]).
+    """
+    import torch
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [M, K]")
+    M, K = x.shape
+    _check(x, "x", torch.bfloat16, (M, K))
+    if codes is None:
+        codes = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((M, K // 32), dtype=torch.uint8, device=x.device)
+    _check(codes, "codes", torch.uint8, (M, K // 2))
+    _check(scales, "scales", torch.uint8, (M, K // 32))
+    rc = mxfp4_quantize_sr(x.data_ptr(), M, K, _seed(seed), codes.data_ptr(), scales.data_ptr(),
+                           _stream_handle(stream))
+    if rc != 0:
+        raise Mxfp4Error(rc, "mxfp4_quantize_sr")
+    return codes, scales
+
+
+def quantize_2d_sr(x, seed, stream=None):
+    """Row-wise and column-wise BF16 -> MXFP4 with stochastic rounding.
+
+    Returns (codes [M, K/2], scales [M, K/32], codes_t [K, M/2], scales_t
+    [K, M/32]), uint8.
+    """
+    import torch
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [M, K]")
+    M, K = x.shape
+    _check(x, "x", torch.bfloat16, (M, K))
+    dev = x.device
+    codes = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((M, K // 32), dtype=torch.uint8, device=dev)
+    codes_t = torch.empty((K, M // 2), dtype=torch.uint8, device=dev)
+    scales_t = torch.empty((K, M // 32), dtype=torch.uint8, device=dev)
+    rc = mxfp4_quantize_2d_sr(x.data_ptr(), M, K, _seed(seed), codes.data_ptr(),
+                              scales.data_ptr(), codes_t.data_ptr(), scales_t.data_ptr(),
+                              _stream_handle(stream))
+    if rc != 0:
+        raise Mxfp4Error(rc, "mxfp4_quantize_2d_sr")
     return codes, scales, codes_t, scales_t
 
 

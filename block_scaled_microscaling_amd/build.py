@@ -13,7 +13,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmxfp4.so")
-SOURCES = ["api.hip", "quantize.hip", "quantize2d.hip", "gemm.hip", "gemm_skinny.hip"]
+SOURCES = ["api.hip", "quantize.hip", "quantize_sr.hip", "quantize2d.hip", "gemm.hip",
+           "gemm_skinny.hip"]
 ARCH = "gfx950"
 
 

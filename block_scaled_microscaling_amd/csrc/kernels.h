@@ -17,6 +17,14 @@ hipError_t launch_quantize(const void* x_bf16, int64_t nblocks, void* codes, voi
 hipError_t launch_quantize_2d(const void* x_bf16, int M, int K, void* codes_row, void* scales_row,
                               void* codes_col, void* scales_col, hipStream_t stream);
 
+// Stochastic-rounding variants (Philox4x32-10 keyed by block coordinates,
+// direction and `seed`): row-wise over [M, K], and both forms of X [M, K].
+hipError_t launch_quantize_sr(const void* x_bf16, int64_t M, int64_t K, uint64_t seed,
+                              void* codes, void* scales, hipStream_t stream);
+hipError_t launch_quantize_2d_sr(const void* x_bf16, int M, int K, uint64_t seed, void* codes_row,
+                                 void* scales_row, void* codes_col, void* scales_col,
+                                 hipStream_t stream);
+
 // C[M,N] = A[M,K] * B[N,K]^T with block scales; out_fp32 selects FP32 vs BF16.
 hipError_t launch_gemm(const void* A, const void* As, const void* B, const void* Bs, int M,
                        int N, int K, bool out_fp32, void* C, hipStream_t stream);

@@ -24,10 +24,19 @@
 //   LDS again and written with 8 lanes per 128-byte column segment: whole
 //   cache lines per store.
 // Edge tiles (M or K not multiples of the tile) mask whole 32-element blocks.
+//
+// The stochastic-rounding variant (kSR) keeps the mapping and replaces only
+// the element rounding (stochastic.h). Row phase: loads go in pairs and the
+// two lanes of a half block split the draws as in quantize_sr.hip (the even
+// lane draws for load 2g, the odd lane for 2g + 1, one DPP swap). Column
+// phase: each thread owns whole column blocks and takes both draws of each,
+// keyed with direction 1, the column of X as the row and the block index
+// along M as the block column.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "kernels.h"
+#include "stochastic.h"
 
 namespace mxfp4 {
 namespace {
@@ -69,10 +78,15 @@ __device__ __forceinline__ uint32_t quad_max(uint32_t v) {
   return max(v, o);
 }
 
+__device__ __forceinline__ uint32_t swap_pair(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);
+}
+
+template <bool kSR>
 __global__ __launch_bounds__(kThreads) void quantize_2d_kernel(
     const uint8_t* __restrict__ x, int M, int K, uint8_t* __restrict__ codes_row,
     uint8_t* __restrict__ scales_row, uint8_t* __restrict__ codes_col,
-    uint8_t* __restrict__ scales_col) {
+    uint8_t* __restrict__ scales_col, uint32_t key0, uint32_t key1) {
   __shared__ __align__(16) uint8_t tile[kRows * kLdsRow];
   const int t = threadIdx.x;
   const int m0 = blockIdx.y * kRows;
@@ -92,6 +106,8 @@ __global__ __launch_bounds__(kThreads) void quantize_2d_kernel(
                        reinterpret_cast<const u32x4_t*>(x + m * row_bytes + 2 * (int64_t)col))
                  : u32x4_t{0u, 0u, 0u, 0u};
     }
+    const int odd = t & 1;
+    uint32_t rnd_next[2] = {0u, 0u};  // kSR: the odd load's bytes of a pair
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int r = 16 * i + (t >> 4);
@@ -101,7 +117,28 @@ __global__ __launch_bounds__(kThreads) void quantize_2d_kernel(
                               max2(abs_pair(q[2]), abs_pair(q[3])));
       const uint32_t amax = quad_max(max((uint32_t)mx.x, (uint32_t)mx.y));
       const uint32_t byte = scale_byte(amax);
-      const uint32_t c = encode8(q[0], q[1], q[2], q[3], __uint_as_float(byte << 23));
+      uint32_t c;
+      if constexpr (kSR) {
+        // Draws for the pair of loads (i, i + 1), taken at the even one.
+        uint32_t rnd[2];
+        if ((i & 1) == 0) {
+          const uint32_t drow = (uint32_t)(m0 + 16 * (i + odd) + (t >> 4));
+          const Draw d = philox4x32_10((uint32_t)(col / 32), drow, kDirRowwise,
+                                       (uint32_t)((t >> 1) & 1), key0, key1);
+          const uint32_t got0 = swap_pair(odd ? d.w[0] : d.w[2]);
+          const uint32_t got1 = swap_pair(odd ? d.w[1] : d.w[3]);
+          rnd[0] = odd ? got0 : d.w[0];
+          rnd[1] = odd ? got1 : d.w[1];
+          rnd_next[0] = odd ? d.w[2] : got0;
+          rnd_next[1] = odd ? d.w[3] : got1;
+        } else {
+          rnd[0] = rnd_next[0];
+          rnd[1] = rnd_next[1];
+        }
+        c = sr_encode8(q[0], q[1], q[2], q[3], 1 - (int)byte, rnd[0], rnd[1]);
+      } else {
+        c = encode8(q[0], q[1], q[2], q[3], __uint_as_float(byte << 23));
+      }
       const int m = m0 + r;
       if (m < M && col < K) {
         *reinterpret_cast<uint32_t*>(codes_row + (int64_t)m * (K / 2) + col / 2) = c;
@@ -131,17 +168,35 @@ __global__ __launch_bounds__(kThreads) void quantize_2d_kernel(
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const uint32_t byte = scale_byte(e == 0 ? (uint32_t)mx.x : (uint32_t)mx.y);
-      const float scale = __uint_as_float(byte << 23);
-      const uint32_t sel = e == 0 ? 0x05040100u : 0x07060302u;
+      if constexpr (kSR) {
+        // Block (column c0 + 2 cp + e of X, row block m0 / 32 + rb): draw h
+        // covers its rows 16 h .. 16 h + 15.
+        const uint32_t kcol = (uint32_t)(c0 + 2 * cp + e);
+        const uint32_t jblk = (uint32_t)(m0 / 32 + rb);
+        const Draw d[2] = {philox4x32_10(jblk, kcol, kDirColumnwise, 0u, key0, key1),
+                           philox4x32_10(jblk, kcol, kDirColumnwise, 1u, key0, key1)};
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        uint32_t p[4];
+        for (int g = 0; g < 4; ++g) {
+          uint32_t xs[8];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int i = 8 * g + 2 * j;
-          p[j] = __builtin_amdgcn_perm(w[i + 1], w[i], sel);
+          for (int i = 0; i < 8; ++i)
+            xs[i] = e == 0 ? w[8 * g + i] << 16 : w[8 * g + i] & 0xFFFF0000u;
+          out[rbi][e][g] = sr_encode8_f32(xs, 1 - (int)byte, d[g >> 1].w[2 * (g & 1)],
+                                          d[g >> 1].w[2 * (g & 1) + 1]);
         }
-        out[rbi][e][g] = encode8(p[0], p[1], p[2], p[3], scale);
+      } else {
+        const float scale = __uint_as_float(byte << 23);
+        const uint32_t sel = e == 0 ? 0x05040100u : 0x07060302u;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          uint32_t p[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int i = 8 * g + 2 * j;
+            p[j] = __builtin_amdgcn_perm(w[i + 1], w[i], sel);
+          }
+          out[rbi][e][g] = encode8(p[0], p[1], p[2], p[3], scale);
+        }
       }
       sbyte[rbi][e] = byte;
     }
@@ -195,10 +250,22 @@ __global__ __launch_bounds__(kThreads) void quantize_2d_kernel(
 hipError_t launch_quantize_2d(const void* x_bf16, int M, int K, void* codes_row, void* scales_row,
                               void* codes_col, void* scales_col, hipStream_t stream) {
   const dim3 grid((K + kCols - 1) / kCols, (M + kRows - 1) / kRows);
-  hipLaunchKernelGGL(quantize_2d_kernel, grid, dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL(quantize_2d_kernel<false>, grid, dim3(kThreads), 0, stream,
                      static_cast<const uint8_t*>(x_bf16), M, K,
                      static_cast<uint8_t*>(codes_row), static_cast<uint8_t*>(scales_row),
-                     static_cast<uint8_t*>(codes_col), static_cast<uint8_t*>(scales_col));
+                     static_cast<uint8_t*>(codes_col), static_cast<uint8_t*>(scales_col), 0u, 0u);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_2d_sr(const void* x_bf16, int M, int K, uint64_t seed, void* codes_row,
+                                 void* scales_row, void* codes_col, void* scales_col,
+                                 hipStream_t stream) {
+  const dim3 grid((K + kCols - 1) / kCols, (M + kRows - 1) / kRows);
+  hipLaunchKernelGGL(quantize_2d_kernel<true>, grid, dim3(kThreads), 0, stream,
+                     static_cast<const uint8_t*>(x_bf16), M, K,
+                     static_cast<uint8_t*>(codes_row), static_cast<uint8_t*>(scales_row),
+                     static_cast<uint8_t*>(codes_col), static_cast<uint8_t*>(scales_col),
+                     (uint32_t)seed, (uint32_t)(seed >> 32));
   return hipGetLastError();
 }
 

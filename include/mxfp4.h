@@ -1,6 +1,7 @@
 /*
- * mxfp4.h -- C ABI of libmxfp4.so: row-wise BF16 -> MXFP4 quantize and the
- * block-scaled MXFP4 x MXFP4 ("a4w4") GEMM on AMD Instinct gfx950 (MI355X).
+ * mxfp4.h -- C ABI of libmxfp4.so: BF16 -> MXFP4 quantize (row-wise or
+ * bidimensional, round-to-nearest or stochastic) and the block-scaled
+ * MXFP4 x MXFP4 ("a4w4") GEMM on AMD Instinct gfx950 (MI355X).
  *
  * Format ("Integrate MXFP4 hipblaslt GEMM support", ROCm/TransformerEngine
  * #697, Changes list): an MXFP4 operand is FP4 E2M1 elements with one UE8M0
@@ -83,6 +84,31 @@ int mxfp4_quantize_async(const void* x_bf16, int64_t M, int64_t K, void* codes_o
  * Asynchronous on `stream` (a hipStream_t, or NULL for the null stream). */
 int mxfp4_quantize_2d(const void* x_bf16, int64_t M, int64_t K, void* codes_row,
                       void* scales_row, void* codes_col, void* scales_col, void* stream);
+
+/* Stochastic-rounding quantize. Scales exactly as mxfp4_quantize; each code
+ * rounds |x| / 2^e to one of its two E2M1 neighbours lo <= |x|/2^e < hi at
+ * random: with frac = (|x|/2^e - lo) / (hi - lo) and u the element's random
+ * byte, the result is hi when floor(256 frac) + u >= 256, else lo (so hi
+ * with probability floor(256 frac) / 256, which is frac whenever
+ * |x|/2^e >= 1/4); |x|/2^e >= 6 gives 6; the sign bit is kept. The random
+ * bytes follow the stochastic-rounding design described on
+ * NVIDIA/TransformerEngine #3809 (description): one Philox4x32-10 draw
+ * (Salmon et al., SC'11) per 16-element half block h of block j of output
+ * row r in direction d (0 = row-wise), counter (j, r, d, h), key (seed low
+ * 32 bits, seed high 32 bits); element 16 h + i takes byte i % 4, least
+ * significant first, of word i / 4. Equal arguments give equal bytes.
+ * Arguments, layouts, requirements and errors as mxfp4_quantize_async. */
+int mxfp4_quantize_sr(const void* x_bf16, int64_t M, int64_t K, uint64_t seed,
+                      void* codes_out, void* scales_out, void* stream);
+
+/* Bidimensional quantize with stochastic rounding: the row-wise outputs are
+ * mxfp4_quantize_sr(x, seed) and the column-wise ones are the row-wise
+ * stochastic quantize of X^T with direction d = 1 (output row r = column k
+ * of X, j = block index along M). Arguments, layouts, requirements and
+ * errors as mxfp4_quantize_2d. */
+int mxfp4_quantize_2d_sr(const void* x_bf16, int64_t M, int64_t K, uint64_t seed,
+                         void* codes_row, void* scales_row, void* codes_col,
+                         void* scales_col, void* stream);
 
 /* Block-scaled GEMM, TN: C[m, n] = sum_k dq(A[m, k]) * dq(B[n, k]) with
  * dq(code, scale) = E2M1(code) * 2^(scale - 127), fp32 accumulation; the

@@ -32,7 +32,8 @@ def test_library_exports_every_declared_symbol():
     lib = mx.load_library()
     names = _declared_functions()
     assert names == ["mxfp4_available", "mxfp4_gemm", "mxfp4_quantize",
-                     "mxfp4_quantize_2d", "mxfp4_quantize_async", "mxfp4_strerror"]
+                     "mxfp4_quantize_2d", "mxfp4_quantize_2d_sr", "mxfp4_quantize_async",
+                     "mxfp4_quantize_sr", "mxfp4_strerror"]
     for n in names:
         assert hasattr(lib, n), n
 
@@ -84,6 +85,7 @@ def test_gemm_rejects_misaligned():
 def test_quantize_rejects_bad_sizes(M, K):
     assert mx.mxfp4_quantize(P16, M, K, P16, P16) == EINVAL
     assert mx.mxfp4_quantize_async(P16, M, K, P16, P16, None) == EINVAL
+    assert mx.mxfp4_quantize_sr(P16, M, K, 7, P16, P16, None) == EINVAL
 
 
 def test_quantize_rejects_nulls_and_misalignment():
@@ -92,12 +94,18 @@ def test_quantize_rejects_nulls_and_misalignment():
     assert mx.mxfp4_quantize(P16, 4, 32, P16, None) == EINVAL
     assert mx.mxfp4_quantize(P16 + 8, 4, 32, P16, P16) == EALIGN
     assert mx.mxfp4_quantize(P16, 4, 32, P16 + 2, P16) == EALIGN
+    assert mx.mxfp4_quantize_sr(None, 4, 32, 1, P16, P16, None) == EINVAL
+    assert mx.mxfp4_quantize_sr(P16, 4, 32, 1, None, P16, None) == EINVAL
+    assert mx.mxfp4_quantize_sr(P16, 4, 32, 1, P16, None, None) == EINVAL
+    assert mx.mxfp4_quantize_sr(P16 + 8, 4, 32, 1, P16, P16, None) == EALIGN
+    assert mx.mxfp4_quantize_sr(P16, 4, 32, 1, P16 + 2, P16, None) == EALIGN
 
 
 @pytest.mark.parametrize("M,K", [(0, 32), (32, 0), (16, 32), (32, 16), (48, 64), (64, 48),
                                  (1 << 31, 32), (1 << 20, 1 << 20)])
 def test_quantize_2d_rejects_bad_sizes(M, K):
     assert mx.mxfp4_quantize_2d(P16, M, K, P16, P16, P16, P16, None) == EINVAL
+    assert mx.mxfp4_quantize_2d_sr(P16, M, K, 3, P16, P16, P16, P16, None) == EINVAL
 
 
 def test_quantize_2d_rejects_nulls_and_misalignment():
@@ -110,6 +118,15 @@ def test_quantize_2d_rejects_nulls_and_misalignment():
         bad = list(args)
         bad[i] = P16 + 8
         assert mx.mxfp4_quantize_2d(*bad) == EALIGN
+    sr_args = [P16, 64, 64, 2**64 - 1, P16, P16, P16, P16, None]
+    for i in (0, 4, 5, 6, 7):
+        bad = list(sr_args)
+        bad[i] = None
+        assert mx.mxfp4_quantize_2d_sr(*bad) == EINVAL
+    for i in (0, 4, 6):
+        bad = list(sr_args)
+        bad[i] = P16 + 8
+        assert mx.mxfp4_quantize_2d_sr(*bad) == EALIGN
 
 
 def test_no_device_reports_unsupported():
@@ -119,6 +136,8 @@ def test_no_device_reports_unsupported():
     assert mx.mxfp4_gemm(P16, P16, P16, P16, 32, 32, 256, mx.OUT_BF16, P16, None) == EUNSUPPORTED
     assert mx.mxfp4_quantize(P16, 4, 32, P16, P16) == EUNSUPPORTED
     assert mx.mxfp4_quantize_2d(P16, 32, 32, P16, P16, P16, P16, None) == EUNSUPPORTED
+    assert mx.mxfp4_quantize_sr(P16, 4, 32, 5, P16, P16, None) == EUNSUPPORTED
+    assert mx.mxfp4_quantize_2d_sr(P16, 32, 32, 5, P16, P16, P16, P16, None) == EUNSUPPORTED
 
 
 def test_tensor_layer_validates_before_calling():
@@ -128,3 +147,7 @@ def test_tensor_layer_validates_before_calling():
         mx.quantize(x)
     with pytest.raises(ValueError):
         mx.quantize(torch.zeros(4, dtype=torch.bfloat16))
+    with pytest.raises(TypeError):
+        mx.quantize_sr(x, 1)
+    with pytest.raises(ValueError):
+        mx.quantize_sr(torch.zeros((4, 64), dtype=torch.bfloat16), -1)
