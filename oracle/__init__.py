@@ -31,6 +31,10 @@ from .stochastic import (  # noqa: F401
     quantize_sr,
     quantize_2d_sr,
 )
+from .swiglu import (  # noqa: F401
+    silu,
+    swiglu_reference,
+)
 from .compare import (  # noqa: F401
     FP32_REL_TOL,
     round_to_bf16,
@@ -39,4 +43,5 @@ from .compare import (  # noqa: F401
     bf16_ulp,
     check_fp32,
     check_bf16,
+    check_act_bf16,
 )

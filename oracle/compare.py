@@ -79,3 +79,11 @@ def check_bf16(out_bits, c_ref, s_ref, rel_tol=FP32_REL_TOL):
     c_out = (out_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     near = np.abs(c_out - c_ref) <= rel_tol * np.asarray(s_ref) + 0.5 * bf16_ulp(c_out)
     return literal, literal | near
+
+
+def check_act_bf16(act_bits, act_ref, tol):
+    """Mask: a BF16 activation output within tol + half a BF16 step of the
+    float64 reference (the fused SwiGLU's act, oracle.swiglu)."""
+    act_bits = np.asarray(act_bits, dtype=np.uint16)
+    got = (act_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return np.abs(got - act_ref) <= np.asarray(tol) + 0.5 * bf16_ulp(got)
