@@ -46,6 +46,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="square")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-swiglu", action="store_true",
+                   help="skip timing the fused SwiGLU gate+up GEMM at the Llama MLP shape")
     p.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "gemm_traffic.json"),
                    help="HBM bytes per GEMM launch from rocprofv3 counters, if measured")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -110,6 +112,51 @@ def cpu_baseline(a_bits, b_bits, K, rows=8192, cols=8192):
         "sample": (f"C block {rows}x{cols} over K={K}: oracle quantize of {rows}+{cols} rows, "
                    f"float64 dequantize, C and S matmuls; {dt:.2f} s wall"),
     }
+
+
+def time_swiglu(mx, torch, dev, stream, reps=10):
+    """The gate+up GEMM of the Llama-3-8B MLP shape (16384 x 28672 x 4096)
+    with its fused SwiGLU + MXFP4 requantize epilogue, timed alone, beside
+    the plain GEMM of the same shape writing its 940 MB BF16 C."""
+    from synth import WORKLOADS, bf16_matrix
+    w = WORKLOADS["mlp_gate_up"]
+    M, N, K = w.M, w.N, w.K
+    print(f"bench: fused SwiGLU gate+up {M}x{N}x{K}", file=sys.stderr, flush=True)
+    a = torch.from_numpy(bf16_matrix((M, K), w.a_dist, w.a_seed).view(np.int16))
+    ac, as_ = mx.quantize(a.view(torch.bfloat16).to(dev))
+    b = torch.from_numpy(bf16_matrix((N, K), w.b_dist, w.b_seed).view(np.int16))
+    bc, bs = mx.quantize(b.view(torch.bfloat16).to(dev))
+    del a, b
+    Nh = N // 2
+    codes = torch.empty((M, Nh // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((M, Nh // 32), dtype=torch.uint8, device=dev)
+    c = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+
+    def fused():
+        rc = mx.mxfp4_gemm_swiglu(ac.data_ptr(), as_.data_ptr(), bc.data_ptr(), bs.data_ptr(),
+                                  M, N, K, codes.data_ptr(), scales.data_ptr(), None,
+                                  stream.cuda_stream)
+        if rc != 0:
+            raise mx.Mxfp4Error(rc, "mxfp4_gemm_swiglu")
+
+    def plain():
+        mx.gemm(ac, as_, bc, bs, out=c)
+
+    out = {"shape": f"{M}x{N}x{K}"}
+    for name, fn in (("fused", fused), ("plain_bf16_gemm", plain)):
+        for _ in range(2):
+            fn()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        out[name + "_ms"] = ms
+        out[name + "_tflops"] = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+    return out
 
 
 def main():
@@ -286,6 +333,8 @@ def main():
         "b_copies_rotated": copies,
         "roofline": roofline,
     }
+    if not args.no_swiglu:
+        result["swiglu_gate_up"] = time_swiglu(mx, torch, dev, stream)
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(a_bits, b_bits, K)

@@ -6,10 +6,11 @@ marshals arguments. PyTorch supplies device memory and streams.
 
 Two layers, same names as the C ABI:
   * mxfp4_available, mxfp4_strerror, mxfp4_quantize, mxfp4_quantize_async,
-    mxfp4_quantize_2d, mxfp4_quantize_sr, mxfp4_quantize_2d_sr, mxfp4_gemm
-    take raw device pointers (ints) and return the C status code.
+    mxfp4_quantize_2d, mxfp4_quantize_sr, mxfp4_quantize_2d_sr, mxfp4_gemm,
+    mxfp4_gemm_swiglu take raw device pointers (ints) and return the C
+    status code.
   * quantize(x), quantize_2d(x), quantize_sr(x, seed), quantize_2d_sr(x,
-    seed) and gemm(...) take torch tensors, check their dtype, device,
+    seed), gemm(...) and gemm_swiglu(...) take torch tensors, check their dtype, device,
     shape and contiguity, allocate outputs when none are given, enqueue on
     torch's current stream and raise Mxfp4Error on a non-zero status.
 
@@ -23,7 +24,8 @@ __all__ = [
     "Mxfp4Error", "OUT_BF16", "OUT_FP32", "library_path", "load_library",
     "mxfp4_available", "mxfp4_strerror", "mxfp4_quantize", "mxfp4_quantize_async",
     "mxfp4_quantize_2d", "mxfp4_quantize_sr", "mxfp4_quantize_2d_sr", "mxfp4_gemm",
-    "quantize", "quantize_2d", "quantize_sr", "quantize_2d_sr", "gemm",
+    "mxfp4_gemm_swiglu", "quantize", "quantize_2d", "quantize_sr", "quantize_2d_sr", "gemm",
+    "gemm_swiglu",
 ]
 
 OUT_BF16 = 0
@@ -66,6 +68,8 @@ def load_library():
         lib.mxfp4_quantize_2d_sr.restype = i32
         lib.mxfp4_gemm.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, vp, vp]
         lib.mxfp4_gemm.restype = i32
+        lib.mxfp4_gemm_swiglu.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, vp, vp, vp]
+        lib.mxfp4_gemm_swiglu.restype = i32
         _lib = lib
     return _lib
 
@@ -106,6 +110,12 @@ def mxfp4_quantize_2d_sr(x_bf16, M, K, seed, codes_row, scales_row, codes_col, s
 def mxfp4_gemm(A_codes, A_scales, B_codes, B_scales, M, N, K, out_dtype, C, stream):
     return int(load_library().mxfp4_gemm(A_codes, A_scales, B_codes, B_scales, M, N, K,
                                          out_dtype, C, stream))
+
+
+def mxfp4_gemm_swiglu(A_codes, A_scales, B_codes, B_scales, M, N, K, act_codes, act_scales,
+                      act_bf16, stream):
+    return int(load_library().mxfp4_gemm_swiglu(A_codes, A_scales, B_codes, B_scales, M, N, K,
+                                                act_codes, act_scales, act_bf16, stream))
 
 
 # ------------------------------------------------------- torch tensor layer
@@ -257,3 +267,32 @@ def gemm(A_codes, A_scales, B_codes, B_scales, out_dtype=None, out=None, stream=
     if rc != 0:
         raise Mxfp4Error(rc, "mxfp4_gemm")
     return out
+
+
+def gemm_swiglu(A_codes, A_scales, B_codes, B_scales, want_act=False, stream=None):
+    """Gate+up GEMM with the SwiGLU + MXFP4 requantize epilogue.
+
+    B_codes [N, K/2] / B_scales [N, K/32] hold the stacked [W_gate; W_up]
+    (N/2 rows each). Returns (act_codes uint8 [M, N/4], act_scales uint8
+    [M, N/64]) and, with want_act, also the BF16 act [M, N/2] the codes were
+    quantized from.
+    """
+    import torch
+    M, Kh = A_codes.shape
+    K = 2 * Kh
+    N = B_codes.shape[0]
+    _check(A_codes, "A_codes", torch.uint8, (M, K // 2))
+    _check(A_scales, "A_scales", torch.uint8, (M, K // 32))
+    _check(B_codes, "B_codes", torch.uint8, (N, K // 2))
+    _check(B_scales, "B_scales", torch.uint8, (N, K // 32))
+    dev = A_codes.device
+    Nh = N // 2
+    codes = torch.empty((M, Nh // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((M, max(Nh // 32, 0)), dtype=torch.uint8, device=dev)
+    act = torch.empty((M, Nh), dtype=torch.bfloat16, device=dev) if want_act else None
+    rc = mxfp4_gemm_swiglu(A_codes.data_ptr(), A_scales.data_ptr(), B_codes.data_ptr(),
+                           B_scales.data_ptr(), M, N, K, codes.data_ptr(), scales.data_ptr(),
+                           None if act is None else act.data_ptr(), _stream_handle(stream))
+    if rc != 0:
+        raise Mxfp4Error(rc, "mxfp4_gemm_swiglu")
+    return (codes, scales, act) if want_act else (codes, scales)

@@ -24,6 +24,7 @@ constexpr int kMaxDevices = 64;
 constexpr int64_t kMaxDim = 2147483647;      // 2^31 - 1
 constexpr int64_t kMaxBytes = int64_t(1) << 40;
 constexpr int64_t kMaxGemmK = int64_t(1) << 24;  // per-lane row offsets of the GEMM kernels are 32-bit
+constexpr int64_t kMaxSwigluB = int64_t(1) << 31;
 
 // Per-device state: 0 = not checked yet, 1 = gfx950 and ready, -1 = not usable.
 std::atomic<int> g_device_state[kMaxDevices];
@@ -158,6 +159,28 @@ int mxfp4_gemm(const void* A_codes, const void* A_scales, const void* B_codes,
                                                    (int)N, (int)K, fp32, C, st));
   return launch_status(mxfp4::launch_gemm(A_codes, A_scales, B_codes, B_scales, (int)M, (int)N,
                                           (int)K, fp32, C, st));
+}
+
+int mxfp4_gemm_swiglu(const void* A_codes, const void* A_scales, const void* B_codes,
+                      const void* B_scales, int64_t M, int64_t N, int64_t K, void* act_codes,
+                      void* act_scales, void* act_bf16, void* stream) {
+  if (!A_codes || !A_scales || !B_codes || !B_scales || !act_codes || !act_scales)
+    return MXFP4_EINVAL;
+  if (M <= 0 || N <= 0 || K <= 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim)
+    return MXFP4_EINVAL;
+  if (K % 256 != 0 || M % 32 != 0 || N % 256 != 0 || K > kMaxGemmK) return MXFP4_EINVAL;
+  // The per-lane code offsets of the up half are 32-bit: B's codes < 2 GiB.
+  if (N * (K / 2) >= kMaxSwigluB || M * (K / 2) >= kMaxBytes || M * N >= kMaxBytes)
+    return MXFP4_EINVAL;
+  if (!aligned(A_codes, 16) || !aligned(B_codes, 16) || !aligned(A_scales, 4) ||
+      !aligned(B_scales, 4) || !aligned(act_codes, 16) ||
+      (act_bf16 != nullptr && !aligned(act_bf16, 16)))
+    return MXFP4_EALIGN;
+  const int dev = check_device();
+  if (dev != MXFP4_OK) return dev;
+  return launch_status(mxfp4::launch_gemm_swiglu(A_codes, A_scales, B_codes, B_scales, (int)M,
+                                                 (int)N, (int)K, act_codes, act_scales, act_bf16,
+                                                 static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

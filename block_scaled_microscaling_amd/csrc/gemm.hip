@@ -72,6 +72,12 @@ constexpr int kTileBytes = kTileM * kRowBytes;
 constexpr int kGroupM = 4;
 constexpr int kNumXcd = 8;
 
+// Epilogue modes: C in BF16 or FP32, or the fused SwiGLU + MXFP4 requantize
+// of a gate+up GEMM (see store_tile_swiglu).
+constexpr int kEpiBf16 = 0;
+constexpr int kEpiFp32 = 1;
+constexpr int kEpiSwiglu = 2;
+
 // Scale chunks: kChunk half-steps (128 K each) of scale words for the 256
 // rows of an operand, laid out [half][r][half-step'][tile] for row
 // 128 half + 32 tile + r, where half-step' = half-step ^ ((r >> 1) & 7): the
@@ -123,6 +129,7 @@ struct Ctx {
   const uint8_t* Bs;
   int row_bytes, scale_row_bytes;
   int row0, col0, M, N;
+  int Nh;                 // SwiGLU: activation columns (B rows per half)
   int klast, hlast;
   uint32_t code_lane[2];  // per-lane code DMA offset for row groups at 16 r, 16 r + 8
   const uint8_t* tile_a;  // wave-uniform code bases of this tile, less kDmaBias
@@ -141,6 +148,35 @@ struct Ctx {
   uint32_t s_sel;          // byte-permute selector picking this lane half's bytes
   int wave;
 };
+
+// Global B row of B-tile row t (0..255), clamped into B. With kGlu the tile
+// covers activation columns col0 .. col0 + 127 of a stacked [W_gate; W_up]
+// weight (Nh rows each): tile row t = 128 wx + 32 i + rr (wave column wx,
+// MFMA tile i) is gate row j for even i and up row Nh + j for odd i, where
+// j = col0 + 64 wx + 32 (i / 2) + rr. Each wave then holds the gate and up
+// sums of the same 64 activation columns in matching accumulators. Nh is a
+// multiple of 128, so no row needs clamping, and every per-lane offset built
+// on this map stays an affine function of the lane (per-row clamps cost the
+// K loop about 30 registers, which then spilled around the epilogue).
+template <bool kGlu>
+__device__ __forceinline__ int b_row(const Ctx& c, int t) {
+  if constexpr (kGlu) {
+    return c.col0 + 64 * (t >> 7) + 32 * ((t >> 6) & 1) + (t & 31) + ((t >> 5) & 1) * c.Nh;
+  } else {
+    return min(c.col0 + t, c.N - 1);
+  }
+}
+
+// First global row of the 8-row code group at B-tile rows t .. t + 7
+// (t % 8 == 0), clamped within B (the kGlu map needs no clamp).
+template <bool kGlu>
+__device__ __forceinline__ int b_group_row(const Ctx& c, int t) {
+  if constexpr (kGlu) {
+    return c.col0 + 64 * (t >> 7) + 32 * ((t >> 6) & 1) + (t & 31) + ((t >> 5) & 1) * c.Nh;
+  } else {
+    return min(c.col0 + t, c.N - 8);
+  }
+}
 
 // Code load q (0..7) of this wave's share of K step kt: tile rows
 // 64 w + 8 q .. +7. Lane i lands at row 64 w + 8 q + i / 8, physical chunk
@@ -184,12 +220,11 @@ __device__ __forceinline__ void load_b2(const Ctx& c, Tiles& t, int kt) {
 // (lane / 4) % 8, r = 8 (u % 4) + 2 w + lane / 32, half = u / 4, so
 // row = 128 (u / 4) + 32 (lane % 4) + 8 (u % 4) + 2 w + lane / 32 and the
 // XOR key (r >> 1) & 7 = 4 (u % 2) + w.
-template <int X, int U>
+template <bool kGlu, int X, int U>
 __device__ __forceinline__ void load_scale_part(const Ctx& c, uint8_t* buf, int chunk) {
-  const int origin = X == 0 ? c.row0 : c.col0;
-  const int rows = X == 0 ? c.M : c.N;
   const uint8_t* base = X == 0 ? c.As : c.Bs;
-  const int row = min(origin + 128 * (U / 4) + 8 * (U % 4) + 2 * c.wave + c.scale_lane, rows - 1);
+  const int t_row = 128 * (U / 4) + 8 * (U % 4) + 2 * c.wave + c.scale_lane;
+  const int row = X == 0 ? min(c.row0 + t_row, c.M - 1) : b_row<kGlu>(c, t_row);
   const int t = c.scale_t ^ (4 * (U % 2) + c.wave);
   const int hs = min(kChunk * chunk + t, c.hlast);
   const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(buf) + X * kChunkBytes +
@@ -203,12 +238,11 @@ __device__ __forceinline__ void load_scale_part(const Ctx& c, uint8_t* buf, int 
 // clamped base row. Only for chunks whose 8 half-steps all lie within K; the
 // last chunk of a K that is not a multiple of 1024 takes load_scale_part.
 constexpr int kScaleBias = 1024;
-template <int X, int PP>
+template <bool kGlu, int X, int PP>
 __device__ __forceinline__ void load_scale_pair(const Ctx& c, uint8_t* buf, int chunk) {
-  const int origin = X == 0 ? c.row0 : c.col0;
-  const int rows = X == 0 ? c.M : c.N;
   const uint8_t* base = X == 0 ? c.As : c.Bs;
-  const int row_c = min(origin + 128 * (PP / 2) + 16 * (PP % 2) + 2 * c.wave, rows - 1);
+  const int t_row = 128 * (PP / 2) + 16 * (PP % 2) + 2 * c.wave;
+  const int row_c = X == 0 ? min(c.row0 + t_row, c.M - 1) : b_row<kGlu>(c, t_row);
   // The last steps prefetch chunks past the end of K: those re-read the last
   // chunk (never used) instead of running past the scale rows.
   const int chunk_c = min(chunk, c.hlast / kChunk);
@@ -225,13 +259,13 @@ __device__ __forceinline__ void load_scale_pair(const Ctx& c, uint8_t* buf, int 
 }
 
 // kFull: K is a multiple of 1024, so every chunk is whole.
-template <bool kFull, int X, int PP>
+template <bool kFull, bool kGlu, int X, int PP>
 __device__ __forceinline__ void load_scales2(const Ctx& c, uint8_t* buf, int chunk) {
   if constexpr (kFull) {
-    load_scale_pair<X, PP>(c, buf, chunk);
+    load_scale_pair<kGlu, X, PP>(c, buf, chunk);
   } else {
-    load_scale_part<X, 2 * PP>(c, buf, chunk);
-    load_scale_part<X, 2 * PP + 1>(c, buf, chunk);
+    load_scale_part<kGlu, X, 2 * PP>(c, buf, chunk);
+    load_scale_part<kGlu, X, 2 * PP + 1>(c, buf, chunk);
   }
 }
 
@@ -286,7 +320,7 @@ __device__ __forceinline__ void step_barrier() {
 // T+1: A rows of loads 4..7 and all of B in phases 0-1 (A loads 0..3 came in
 // phase 3 of step T-1). Phase 3 issues step T+2's A loads 0..3 into `cur`
 // and scale parts 2P, 2P+1 of both operands for chunk (T+1)/4 + 1.
-template <bool kFull, int P, int S>
+template <bool kFull, bool kGlu, int P, int S>
 __device__ __forceinline__ void k_step(const Ctx& c0, Tiles& tl,
                                        uint8_t (*chunks)[2 * kChunkBytes], v16f_t (&acc)[4][4],
                                        Frags& fa, Frags& fb, HalfScales& sc0, HalfScales& sc1,
@@ -367,12 +401,12 @@ __device__ __forceinline__ void k_step(const Ctx& c0, Tiles& tl,
   read_frag_b<1 - S>(c, tl, 0, 0, fa.b[0]);
   read_frag_b<1 - S>(c, tl, 0, 1, fa.b[1]);
   load_a2<0, S>(c, tl, ka);
-  load_scales2<kFull, 0, P>(c, pbuf, pchunk);
+  load_scales2<kFull, kGlu, 0, P>(c, pbuf, pchunk);
   MXFP4_FENCE();
   mma_row<3, 1>(acc, fb, sc1);
   read_frag_b<1 - S>(c, tl, 0, 2, fa.b[2]);
   read_frag_b<1 - S>(c, tl, 0, 3, fa.b[3]);
-  load_scales2<kFull, 1, P>(c, pbuf, pchunk);
+  load_scales2<kFull, kGlu, 1, P>(c, pbuf, pchunk);
   MXFP4_FENCE();
   mma_row<3, 2>(acc, fb, sc1);
   read_frag_a<1 - S>(c, tl, 0, 0, fa.a[0]);
@@ -392,6 +426,7 @@ __device__ __forceinline__ void k_step(const Ctx& c0, Tiles& tl,
 
 // Issue the loads that start a tile: K step 0 and scale chunk 0 into slot 0
 // and chunks[0].
+template <bool kGlu>
 __device__ __forceinline__ void issue_tile_head(const Ctx& c0, Tiles& tl,
                                                 uint8_t (*chunks)[2 * kChunkBytes]) {
   Ctx c = c0;
@@ -404,71 +439,74 @@ __device__ __forceinline__ void issue_tile_head(const Ctx& c0, Tiles& tl,
   load_b2<2, 0>(c, tl, 0);
   load_b2<4, 0>(c, tl, 0);
   load_b2<6, 0>(c, tl, 0);
-  load_scale_part<0, 0>(c, chunks[0], 0);
-  load_scale_part<0, 1>(c, chunks[0], 0);
-  load_scale_part<0, 2>(c, chunks[0], 0);
-  load_scale_part<0, 3>(c, chunks[0], 0);
-  load_scale_part<0, 4>(c, chunks[0], 0);
-  load_scale_part<0, 5>(c, chunks[0], 0);
-  load_scale_part<0, 6>(c, chunks[0], 0);
-  load_scale_part<0, 7>(c, chunks[0], 0);
-  load_scale_part<1, 0>(c, chunks[0], 0);
-  load_scale_part<1, 1>(c, chunks[0], 0);
-  load_scale_part<1, 2>(c, chunks[0], 0);
-  load_scale_part<1, 3>(c, chunks[0], 0);
-  load_scale_part<1, 4>(c, chunks[0], 0);
-  load_scale_part<1, 5>(c, chunks[0], 0);
-  load_scale_part<1, 6>(c, chunks[0], 0);
-  load_scale_part<1, 7>(c, chunks[0], 0);
+  load_scale_part<kGlu, 0, 0>(c, chunks[0], 0);
+  load_scale_part<kGlu, 0, 1>(c, chunks[0], 0);
+  load_scale_part<kGlu, 0, 2>(c, chunks[0], 0);
+  load_scale_part<kGlu, 0, 3>(c, chunks[0], 0);
+  load_scale_part<kGlu, 0, 4>(c, chunks[0], 0);
+  load_scale_part<kGlu, 0, 5>(c, chunks[0], 0);
+  load_scale_part<kGlu, 0, 6>(c, chunks[0], 0);
+  load_scale_part<kGlu, 0, 7>(c, chunks[0], 0);
+  load_scale_part<kGlu, 1, 0>(c, chunks[0], 0);
+  load_scale_part<kGlu, 1, 1>(c, chunks[0], 0);
+  load_scale_part<kGlu, 1, 2>(c, chunks[0], 0);
+  load_scale_part<kGlu, 1, 3>(c, chunks[0], 0);
+  load_scale_part<kGlu, 1, 4>(c, chunks[0], 0);
+  load_scale_part<kGlu, 1, 5>(c, chunks[0], 0);
+  load_scale_part<kGlu, 1, 6>(c, chunks[0], 0);
+  load_scale_part<kGlu, 1, 7>(c, chunks[0], 0);
 }
 
 // What phase 3 of step "-1" would have issued: A loads 0..3 of step 1 and
 // parts 0, 1 of chunk 1. Exactly 8 loads: the tile's first wait is vmcnt(8).
+template <bool kGlu>
 __device__ __forceinline__ void issue_tile_tail(const Ctx& c0, Tiles& tl,
                                                 uint8_t (*chunks)[2 * kChunkBytes]) {
   Ctx c = c0;
   asm volatile("" : "+v"(c.scale_lane), "+v"(c.scale_t));
   load_a2<0, 1>(c, tl, min(1, c.klast));
   load_a2<2, 1>(c, tl, min(1, c.klast));
-  load_scale_part<0, 0>(c, chunks[1], 1);
-  load_scale_part<1, 0>(c, chunks[1], 1);
-  load_scale_part<0, 1>(c, chunks[1], 1);
-  load_scale_part<1, 1>(c, chunks[1], 1);
+  load_scale_part<kGlu, 0, 0>(c, chunks[1], 1);
+  load_scale_part<kGlu, 1, 0>(c, chunks[1], 1);
+  load_scale_part<kGlu, 0, 1>(c, chunks[1], 1);
+  load_scale_part<kGlu, 1, 1>(c, chunks[1], 1);
 }
 
-// Point the context at tile id p (XCD-aware order).
+// Point the context at tile id p (XCD-aware order). A SwiGLU tile spans
+// 128 activation columns (256 B rows: 128 gate, 128 up).
+template <bool kGlu>
 __device__ __forceinline__ void set_tile(Ctx& c, int p, int tiles_m, int tiles_n) {
   int tm, tn;
   tile_of(p, tiles_m, tiles_n, tm, tn);
   c.row0 = tm * kTileM;
-  c.col0 = tn * kTileN;
+  c.col0 = tn * (kGlu ? kTileN / 2 : kTileN);
   // Wave's first code row, clamped like the rows of its loads: rows past M
   // (or N) re-read the last 8 rows, computed but never stored.
   const int ra = min(c.row0 + 64 * c.wave, c.M - 8);
-  const int rb = min(c.col0 + 64 * c.wave, c.N - 8);
+  const int rb = b_group_row<kGlu>(c, 64 * c.wave);
   c.tile_a = c.A + (int64_t)ra * c.row_bytes - kDmaBias;
   c.tile_b = c.B + (int64_t)rb * c.row_bytes - kDmaBias;
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
     const int ga = min(c.row0 + 64 * c.wave + 8 * q, c.M - 8) - ra;
-    const int gb = min(c.col0 + 64 * c.wave + 8 * q, c.N - 8) - rb;
+    const int gb = b_group_row<kGlu>(c, 64 * c.wave + 8 * q) - rb;
     c.off_a[q] = (uint32_t)(ga * c.row_bytes) + c.code_lane[q & 1] + kDmaBias - (q % 4) * 1024;
     c.off_b[q] = (uint32_t)(gb * c.row_bytes) + c.code_lane[q & 1] + kDmaBias - (q % 4) * 1024;
   }
-  // Scale pairs: part U = 2p + e of operand X reads row
-  // origin + 128 (U / 4) + 8 (U % 4) + 2 w + scale_lane (clamped), half-step
-  // scale_t ^ (4 e + w); offsets relative to part 2p's clamped first row.
+  // Scale pairs: part U = 2p + e of operand X reads tile row
+  // 128 (U / 4) + 8 (U % 4) + 2 w + scale_lane (its global row clamped),
+  // half-step scale_t ^ (4 e + w); offsets relative to the global row of
+  // part 2p's first tile row (the smallest the pair reads).
 #pragma unroll
   for (int x = 0; x < 2; ++x) {
-    const int origin = x == 0 ? c.row0 : c.col0;
-    const int rows = x == 0 ? c.M : c.N;
 #pragma unroll
     for (int pp = 0; pp < 4; ++pp) {
-      const int row_u = origin + 128 * (pp / 2) + 16 * (pp % 2) + 2 * c.wave;
-      const int row_c = min(row_u, rows - 1);
+      const int tb = 128 * (pp / 2) + 16 * (pp % 2) + 2 * c.wave;
+      const int row_c = x == 0 ? min(c.row0 + tb, c.M - 1) : b_row<kGlu>(c, tb);
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
-        const int lane_row = min(row_u + 8 * e + c.scale_lane, rows - 1) - row_c;
+        const int tr = tb + 8 * e + c.scale_lane;
+        const int lane_row = (x == 0 ? min(c.row0 + tr, c.M - 1) : b_row<kGlu>(c, tr)) - row_c;
         const int t = c.scale_t ^ (4 * e + c.wave);
         c.soff[x][pp][e] =
             (uint32_t)(lane_row * c.scale_row_bytes + 4 * t + kScaleBias - 1024 * e);
@@ -564,11 +602,110 @@ __device__ __forceinline__ void store_tile_bf16_lds(const Ctx& c, v16f_t (&acc)[
   }
 }
 
-template <bool kOutFp32, bool kFull>
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float silu(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+}
+
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two floats -> BF16 pair (round to nearest even) in one conversion.
+__device__ __forceinline__ uint32_t bf16x2_of(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
+}
+
+// SwiGLU + MXFP4 epilogue. Tiles (i, 2 b) and (i, 2 b + 1) of a wave hold
+// the gate and up sums of the same 32 x 32 block of activations
+// act = silu(g) * u (rows row0 + 128 wy + 32 i + r, columns
+// col0 + 64 wx + 32 b + 8 q + 4 h + t for register 4 q + t). act is rounded
+// to BF16 and quantized exactly as the row-wise quantize kernel does, one
+// MX block per (row, b): lanes r and r + 32 hold the two halves of a row's
+// block, so the block amax and the code bytes cross between them once each
+// (v_permlane32_swap). The amax is taken on the fp32 values and rounded
+// once: rounding to BF16 is monotone, so this is the amax of the BF16
+// values. Codes go to act_codes [M, Nh/2], scale bytes to act_scales
+// [M, Nh/32], and the BF16 act to act_bf16 [M, Nh] when given.
+__device__ __forceinline__ void store_tile_swiglu(const int row0, const int col0, const int M,
+                                                  const int Nh, v16f_t (&acc)[4][4], int wy,
+                                                  int wx, int lane, uint8_t* __restrict__ codes,
+                                                  uint8_t* __restrict__ scales,
+                                                  uint16_t* __restrict__ act) {
+  int r = lane & 31, h = lane >> 5;
+  asm volatile("" : "+v"(r), "+v"(h));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m_base = row0 + wy * 128 + i * 32;
+    const int m = m_base + r;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int j0 = col0 + 64 * wx + 32 * b;
+      const bool ok = m_base < M && j0 < Nh;
+      const v16f_t g = acc[i][2 * b];
+      const v16f_t u = acc[i][2 * b + 1];
+      float a[16];
+      float amax = 0.0f;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        a[k] = silu(g[k]) * u[k];
+        amax = fmaxf(amax, fabsf(a[k]));
+      }
+      uint32_t w[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) w[k] = bf16x2_of(a[2 * k], a[2 * k + 1]);
+      if (act != nullptr && ok) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<uint2*>(act + (int64_t)m * Nh + j0 + 8 * q + 4 * h) =
+              make_uint2(w[2 * q], w[2 * q + 1]);
+      }
+      // After the swap each lane holds its own value and its partner's
+      // (lane r + 32 for r < 32, r - 32 otherwise) in the two results.
+      const uint32_t mine = __float_as_uint(amax);
+      const auto both = __builtin_amdgcn_permlane32_swap(mine, mine, false, false);
+      const float bmax = fmaxf(__uint_as_float(both[0]), __uint_as_float(both[1]));
+      const uint32_t mx = bf16x2_of(bmax, 0.0f) & 0x7FFFu;
+      const uint32_t byte = (uint32_t)max((int)(mx >> 7) - 2, 0);
+      const float scale = __uint_as_float(byte << 23);
+      // d[0]: code bytes 4 q' + 2 h + {0, 1} for q' = 0, 1; d[1] for q' = 2, 3.
+      uint32_t d[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        uint32_t x = 0;
+        x = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(x, __builtin_bit_cast(bf16x2_t, w[4 * e]),
+                                                      scale, 0);
+        x = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(
+            x, __builtin_bit_cast(bf16x2_t, w[4 * e + 1]), scale, 1);
+        x = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(
+            x, __builtin_bit_cast(bf16x2_t, w[4 * e + 2]), scale, 2);
+        x = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(
+            x, __builtin_bit_cast(bf16x2_t, w[4 * e + 3]), scale, 3);
+        d[e] = x;
+      }
+      // Lane half h keeps code bytes 8 h .. 8 h + 7 of the block. Swapping
+      // d[0] of the upper lanes with d[1] of the lower ones leaves, in every
+      // lane, the lower lane's word of that byte range in [0] and the upper
+      // lane's in [1].
+      const auto lh = __builtin_amdgcn_permlane32_swap(d[0], d[1], false, false);
+      const uint32_t lo = lh[0], hi = lh[1];
+      if (ok) {
+        *reinterpret_cast<uint2*>(codes + (int64_t)m * (Nh / 2) + j0 / 2 + 8 * h) =
+            make_uint2((lo & 0xFFFFu) | (hi << 16), (lo >> 16) | (hi & 0xFFFF0000u));
+        if (h == 0) scales[(int64_t)m * (Nh / 32) + j0 / 32] = (uint8_t)byte;
+      }
+      MXFP4_FENCE();
+    }
+  }
+}
+
+template <int kEpi, bool kFull>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_tile_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ As,
                       const uint8_t* __restrict__ B, const uint8_t* __restrict__ Bs, int M, int N,
-                      int K, void* __restrict__ C, int tiles_m, int tiles_n) {
+                      int K, void* __restrict__ C, int tiles_m, int tiles_n,
+                      uint8_t* __restrict__ act_codes, uint8_t* __restrict__ act_scales, int Nh) {
+  constexpr bool kGlu = kEpi == kEpiSwiglu;
+  constexpr bool kOutFp32 = kEpi == kEpiFp32;
   __shared__ Tiles tl;
   __shared__ __align__(16) uint8_t chunks[2][2 * kChunkBytes];
 
@@ -591,6 +728,7 @@ void gemm_tile_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__
   c.scale_row_bytes = K / 32;
   c.M = M;
   c.N = N;
+  c.Nh = Nh;
   c.klast = ksteps - 1;
   c.hlast = 2 * ksteps - 1;
   c.wave = wave;
@@ -619,9 +757,9 @@ void gemm_tile_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__
   // Persistent: this workgroup takes tiles blockIdx.x, + gridDim.x, ...; the
   // grid is a multiple of 8, so every tile id keeps its workgroup's XCD.
   int p = blockIdx.x;
-  set_tile(c, p, tiles_m, tiles_n);
-  issue_tile_head(c, tl, chunks);
-  issue_tile_tail(c, tl, chunks);
+  set_tile<kGlu>(c, p, tiles_m, tiles_n);
+  issue_tile_head<kGlu>(c, tl, chunks);
+  issue_tile_tail<kGlu>(c, tl, chunks);
   for (; p < total; p += gridDim.x) {
     asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
 
@@ -641,14 +779,14 @@ void gemm_tile_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__
 
     int T = 0;
     for (; T + 4 <= ksteps; T += 4) {
-      k_step<kFull, 1, 0>(c, tl, chunks, acc, fa, fb, sc0, sc1, T);
-      k_step<kFull, 2, 1>(c, tl, chunks, acc, fa, fb, sc0, sc1, T + 1);
-      k_step<kFull, 3, 0>(c, tl, chunks, acc, fa, fb, sc0, sc1, T + 2);
-      k_step<kFull, 0, 1>(c, tl, chunks, acc, fa, fb, sc0, sc1, T + 3);
+      k_step<kFull, kGlu, 1, 0>(c, tl, chunks, acc, fa, fb, sc0, sc1, T);
+      k_step<kFull, kGlu, 2, 1>(c, tl, chunks, acc, fa, fb, sc0, sc1, T + 1);
+      k_step<kFull, kGlu, 3, 0>(c, tl, chunks, acc, fa, fb, sc0, sc1, T + 2);
+      k_step<kFull, kGlu, 0, 1>(c, tl, chunks, acc, fa, fb, sc0, sc1, T + 3);
     }
-    if (T < ksteps) k_step<kFull, 1, 0>(c, tl, chunks, acc, fa, fb, sc0, sc1, T);
-    if (T + 1 < ksteps) k_step<kFull, 2, 1>(c, tl, chunks, acc, fa, fb, sc0, sc1, T + 1);
-    if (T + 2 < ksteps) k_step<kFull, 3, 0>(c, tl, chunks, acc, fa, fb, sc0, sc1, T + 2);
+    if (T < ksteps) k_step<kFull, kGlu, 1, 0>(c, tl, chunks, acc, fa, fb, sc0, sc1, T);
+    if (T + 1 < ksteps) k_step<kFull, kGlu, 2, 1>(c, tl, chunks, acc, fa, fb, sc0, sc1, T + 1);
+    if (T + 2 < ksteps) k_step<kFull, kGlu, 3, 0>(c, tl, chunks, acc, fa, fb, sc0, sc1, T + 2);
     // Every load of this tile has landed and every LDS read has returned,
     // in all waves, before the next tile's loads reuse the buffers.
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -656,13 +794,21 @@ void gemm_tile_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__
     // Start the next tile's loads, then write this tile's C while they fly;
     // the last 8 loads issued are the ones the next wait leaves outstanding.
     const int pn = p + gridDim.x;
-    if constexpr (kOutFp32) {
+    if constexpr (kGlu) {
+      store_tile_swiglu(c.row0, c.col0, M, Nh, acc, wy, wx, lane, act_codes, act_scales,
+                        static_cast<uint16_t*>(C));
+      if (pn < total) {
+        set_tile<kGlu>(c, pn, tiles_m, tiles_n);
+        issue_tile_head<kGlu>(c, tl, chunks);
+      }
+    } else if constexpr (kOutFp32) {
+      // This epilogue does not touch LDS: the next tile's loads go first.
       const Ctx cur_tile = c;
       if (pn < total) {
-        set_tile(c, pn, tiles_m, tiles_n);
-        issue_tile_head(c, tl, chunks);
+        set_tile<kGlu>(c, pn, tiles_m, tiles_n);
+        issue_tile_head<kGlu>(c, tl, chunks);
       }
-      store_tile<kOutFp32>(cur_tile, acc, wy, wx, r, h, C);
+      store_tile<true>(cur_tile, acc, wy, wx, r, h, C);
     } else {
       // Waves 0, 1 park their blocks in the A slots, waves 2, 3 in the B
       // slots; the next tile's loads wait until every wave has read its
@@ -671,11 +817,11 @@ void gemm_tile_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__
       store_tile_bf16_lds(c, acc, wy, wx, lane, region, C);
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
       if (pn < total) {
-        set_tile(c, pn, tiles_m, tiles_n);
-        issue_tile_head(c, tl, chunks);
+        set_tile<kGlu>(c, pn, tiles_m, tiles_n);
+        issue_tile_head<kGlu>(c, tl, chunks);
       }
     }
-    if (pn < total) issue_tile_tail(c, tl, chunks);
+    if (pn < total) issue_tile_tail<kGlu>(c, tl, chunks);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
@@ -698,18 +844,38 @@ hipError_t init_kernels_for_current_device() {
   return hipSuccess;
 }
 
-hipError_t launch_gemm(const void* A, const void* As, const void* B, const void* Bs, int M, int N,
-                       int K, bool out_fp32, void* C, hipStream_t stream) {
+static hipError_t persistent_workers(int& workers) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  int workers = g_workers[dev].load(std::memory_order_acquire);
+  workers = g_workers[dev].load(std::memory_order_acquire);
   if (workers == 0) {
     e = init_kernels_for_current_device();
     if (e != hipSuccess) return e;
     workers = g_workers[dev].load(std::memory_order_acquire);
   }
+  return hipSuccess;
+}
+
+template <int kEpi>
+static void launch_tile_kernel(bool full, dim3 grid, hipStream_t stream, const uint8_t* a,
+                               const uint8_t* as, const uint8_t* b, const uint8_t* bs, int M,
+                               int N, int K, void* C, int tiles_m, int tiles_n,
+                               uint8_t* act_codes, uint8_t* act_scales, int Nh) {
+  if (full)
+    hipLaunchKernelGGL((gemm_tile_kernel<kEpi, true>), grid, dim3(kThreads), 0, stream, a, as, b,
+                       bs, M, N, K, C, tiles_m, tiles_n, act_codes, act_scales, Nh);
+  else
+    hipLaunchKernelGGL((gemm_tile_kernel<kEpi, false>), grid, dim3(kThreads), 0, stream, a, as, b,
+                       bs, M, N, K, C, tiles_m, tiles_n, act_codes, act_scales, Nh);
+}
+
+hipError_t launch_gemm(const void* A, const void* As, const void* B, const void* Bs, int M, int N,
+                       int K, bool out_fp32, void* C, hipStream_t stream) {
+  int workers = 0;
+  hipError_t e = persistent_workers(workers);
+  if (e != hipSuccess) return e;
   const int tiles_m = (M + kTileM - 1) / kTileM;
   const int tiles_n = (N + kTileN - 1) / kTileN;
   const int total = tiles_m * tiles_n;
@@ -719,18 +885,31 @@ hipError_t launch_gemm(const void* A, const void* As, const void* B, const void*
   const auto* b = static_cast<const uint8_t*>(B);
   const auto* bs = static_cast<const uint8_t*>(Bs);
   const bool full = K % 1024 == 0;
-  if (out_fp32 && full)
-    hipLaunchKernelGGL((gemm_tile_kernel<true, true>), grid, dim3(kThreads), 0, stream, a, as, b,
-                       bs, M, N, K, C, tiles_m, tiles_n);
-  else if (out_fp32)
-    hipLaunchKernelGGL((gemm_tile_kernel<true, false>), grid, dim3(kThreads), 0, stream, a, as, b,
-                       bs, M, N, K, C, tiles_m, tiles_n);
-  else if (full)
-    hipLaunchKernelGGL((gemm_tile_kernel<false, true>), grid, dim3(kThreads), 0, stream, a, as, b,
-                       bs, M, N, K, C, tiles_m, tiles_n);
+  if (out_fp32)
+    launch_tile_kernel<kEpiFp32>(full, grid, stream, a, as, b, bs, M, N, K, C, tiles_m, tiles_n,
+                                 nullptr, nullptr, 0);
   else
-    hipLaunchKernelGGL((gemm_tile_kernel<false, false>), grid, dim3(kThreads), 0, stream, a, as, b,
-                       bs, M, N, K, C, tiles_m, tiles_n);
+    launch_tile_kernel<kEpiBf16>(full, grid, stream, a, as, b, bs, M, N, K, C, tiles_m, tiles_n,
+                                 nullptr, nullptr, 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_swiglu(const void* A, const void* As, const void* B, const void* Bs, int M,
+                              int N, int K, void* act_codes, void* act_scales, void* act_bf16,
+                              hipStream_t stream) {
+  int workers = 0;
+  hipError_t e = persistent_workers(workers);
+  if (e != hipSuccess) return e;
+  const int Nh = N / 2;
+  const int tiles_m = (M + kTileM - 1) / kTileM;
+  const int tiles_n = (Nh + kTileN / 2 - 1) / (kTileN / 2);
+  const int total = tiles_m * tiles_n;
+  const dim3 grid(total < workers ? total : workers);
+  launch_tile_kernel<kEpiSwiglu>(K % 1024 == 0, grid, stream, static_cast<const uint8_t*>(A),
+                                 static_cast<const uint8_t*>(As), static_cast<const uint8_t*>(B),
+                                 static_cast<const uint8_t*>(Bs), M, N, K, act_bf16, tiles_m,
+                                 tiles_n, static_cast<uint8_t*>(act_codes),
+                                 static_cast<uint8_t*>(act_scales), Nh);
   return hipGetLastError();
 }
 

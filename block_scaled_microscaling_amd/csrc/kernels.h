@@ -29,6 +29,13 @@ hipError_t launch_quantize_2d_sr(const void* x_bf16, int M, int K, uint64_t seed
 hipError_t launch_gemm(const void* A, const void* As, const void* B, const void* Bs, int M,
                        int N, int K, bool out_fp32, void* C, hipStream_t stream);
 
+// Gate+up GEMM with the SwiGLU + MXFP4 requantize epilogue: B is the stacked
+// [W_gate; W_up] (N rows, N / 2 each, N % 256 == 0); writes act codes [M, N/4], scales
+// [M, N/64] and, when act_bf16 is not null, the BF16 act [M, N/2].
+hipError_t launch_gemm_swiglu(const void* A, const void* As, const void* B, const void* Bs, int M,
+                              int N, int K, void* act_codes, void* act_scales, void* act_bf16,
+                              hipStream_t stream);
+
 // Same contract, for M up to kSkinnyMaxM: one 32 x 32 tile of C per
 // workgroup, K split between its waves.
 constexpr int kSkinnyMaxM = 128;

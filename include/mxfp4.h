@@ -130,6 +130,30 @@ int mxfp4_gemm(const void* A_codes, const void* A_scales, const void* B_codes,
                const void* B_scales, int64_t M, int64_t N, int64_t K, int out_dtype,
                void* C, void* stream);
 
+/* Gate+up GEMM of a SwiGLU MLP with the activation fused into its epilogue
+ * and requantized to MXFP4 for the down projection. B holds the stacked
+ * weight [W_gate; W_up]: rows 0 .. N/2 - 1 are W_gate, rows N/2 .. N - 1
+ * W_up (Nh = N/2 activation columns). With g = A W_gate^T and u = A W_up^T
+ * (the sums of mxfp4_gemm, fp32), the kernel computes
+ *   act[m, j] = silu(g[m, j]) * u[m, j],  silu(z) = z / (1 + exp(-z))
+ * (SwiGLU: Shazeer, "GLU Variants Improve Transformer", 2020) in fp32,
+ * rounds act to BF16 (nearest even) and quantizes it exactly as
+ * mxfp4_quantize does, blocks of 32 along j. The MXFP4 GEMM of "Integrate
+ * MXFP4 hipblaslt GEMM support" (#697, Changes list) has no activation
+ * epilogue; this entry point widens it. C [M, N] is never written.
+ * A_codes [M, K/2], B_codes [N, K/2]: 16-byte aligned
+ * A_scales [M, K/32], B_scales [N, K/32]: 4-byte aligned
+ * act_codes [M, Nh/2] uint8, 16-byte aligned; act_scales [M, Nh/32] uint8
+ * act_bf16 [M, Nh] BF16, 16-byte aligned, or NULL to skip writing it
+ * Requires K % 256 == 0, M % 32 == 0, N % 256 == 0 (the kernel's tiles
+ * cover 128 activation columns and never straddle the gate/up boundary),
+ * M, N, K > 0, K <= 2^24,
+ * N * K / 2 < 2^31 (B's codes under 2 GiB), M * N < 2^40; otherwise
+ * MXFP4_EINVAL (MXFP4_EALIGN for alignment) and nothing is launched. */
+int mxfp4_gemm_swiglu(const void* A_codes, const void* A_scales, const void* B_codes,
+                      const void* B_scales, int64_t M, int64_t N, int64_t K, void* act_codes,
+                      void* act_scales, void* act_bf16, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -31,7 +31,7 @@ def _declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = mx.load_library()
     names = _declared_functions()
-    assert names == ["mxfp4_available", "mxfp4_gemm", "mxfp4_quantize",
+    assert names == ["mxfp4_available", "mxfp4_gemm", "mxfp4_gemm_swiglu", "mxfp4_quantize",
                      "mxfp4_quantize_2d", "mxfp4_quantize_2d_sr", "mxfp4_quantize_async",
                      "mxfp4_quantize_sr", "mxfp4_strerror"]
     for n in names:
@@ -61,6 +61,26 @@ def test_gemm_rejects_bad_dtype_and_nulls():
         ptrs[i] = None
         a, as_, b, bs, c = ptrs
         assert mx.mxfp4_gemm(a, as_, b, bs, 32, 32, 256, mx.OUT_FP32, c, None) == EINVAL
+
+
+@pytest.mark.parametrize("M,N,K", [
+    (0, 256, 256), (32, 0, 256), (32, 256, 0), (33, 256, 256), (32, 96, 256), (32, 64, 256),
+    (32, 384, 256), (32, 256, 128), (32, 256, (1 << 24) + 256), (32, 1 << 14, 1 << 18),
+])
+def test_gemm_swiglu_rejects_bad_sizes(M, N, K):
+    assert mx.mxfp4_gemm_swiglu(P16, P16, P16, P16, M, N, K, P16, P16, None, None) == EINVAL
+
+
+def test_gemm_swiglu_rejects_nulls_and_misalignment():
+    args = [P16, P16, P16, P16, 64, 256, 256, P16, P16, P16, None]
+    for i in (0, 1, 2, 3, 7, 8):
+        bad = list(args)
+        bad[i] = None
+        assert mx.mxfp4_gemm_swiglu(*bad) == EINVAL
+    for i, off in ((0, 8), (2, 8), (1, 2), (3, 1), (7, 8), (9, 8)):
+        bad = list(args)
+        bad[i] = P16 + off
+        assert mx.mxfp4_gemm_swiglu(*bad) == EALIGN, i
 
 
 def test_gemm_rejects_oversized_buffers():
@@ -137,6 +157,8 @@ def test_no_device_reports_unsupported():
     assert mx.mxfp4_quantize(P16, 4, 32, P16, P16) == EUNSUPPORTED
     assert mx.mxfp4_quantize_2d(P16, 32, 32, P16, P16, P16, P16, None) == EUNSUPPORTED
     assert mx.mxfp4_quantize_sr(P16, 4, 32, 5, P16, P16, None) == EUNSUPPORTED
+    assert mx.mxfp4_gemm_swiglu(P16, P16, P16, P16, 32, 256, 256, P16, P16, None,
+                                None) == EUNSUPPORTED
     assert mx.mxfp4_quantize_2d_sr(P16, 32, 32, 5, P16, P16, P16, P16, None) == EUNSUPPORTED
 
 
