@@ -35,6 +35,11 @@ from .swiglu import (  # noqa: F401
     silu,
     swiglu_reference,
 )
+from .shuffle import (  # noqa: F401
+    shuffled_sizes,
+    shuffle_b,
+    unshuffle_b,
+)
 from .compare import (  # noqa: F401
     FP32_REL_TOL,
     round_to_bf16,
