@@ -275,6 +275,14 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / 20
 
+    # The same GEMM with B pre-shuffled once (mxfp4_shuffle_b), timed alone.
+    bsh_c, bsh_s = mx.shuffle_b(bc, bs)
+    gsh_ms = time_alone(lambda: mx.mxfp4_gemm_bshuffled(ac.data_ptr(), as_.data_ptr(),
+                                                        bsh_c.data_ptr(), bsh_s.data_ptr(), M, N,
+                                                        K, w.out_dtype, c.data_ptr(),
+                                                        stream.cuda_stream),
+                        "mxfp4_gemm_bshuffled")
+
     seed = 0x5EED
     qsr_ms = time_alone(lambda: mx.mxfp4_quantize_sr(x.data_ptr(), M, K, seed, ac.data_ptr(),
                                                      as_.data_ptr(), stream.cuda_stream),
@@ -334,6 +342,8 @@ def main():
         "quantize_gbps": quant_gbps,
         "quantize_ms": float(q_ms.mean()),
         "quantize_hbm_frac": quant_gbps / HBM_PEAK_GBPS,
+        "gemm_bshuffled_ms": gsh_ms,
+        "gemm_bshuffled_tflops": flops / (gsh_ms * 1e-3) / 1e12,
         "quantize_sr_ms": qsr_ms,
         "quantize_sr_gbps": gbps(q_bytes, qsr_ms),
         "quantize_2d_ms": q2_ms,

@@ -25,7 +25,8 @@ __all__ = [
     "mxfp4_available", "mxfp4_strerror", "mxfp4_quantize", "mxfp4_quantize_async",
     "mxfp4_quantize_2d", "mxfp4_quantize_sr", "mxfp4_quantize_2d_sr", "mxfp4_gemm",
     "mxfp4_gemm_swiglu", "quantize", "quantize_2d", "quantize_sr", "quantize_2d_sr", "gemm",
-    "gemm_swiglu",
+    "gemm_swiglu", "mxfp4_shuffle_b_sizes", "mxfp4_shuffle_b", "mxfp4_gemm_bshuffled",
+    "shuffle_b", "gemm_bshuffled",
 ]
 
 OUT_BF16 = 0
@@ -70,6 +71,12 @@ def load_library():
         lib.mxfp4_gemm.restype = i32
         lib.mxfp4_gemm_swiglu.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, vp, vp, vp]
         lib.mxfp4_gemm_swiglu.restype = i32
+        lib.mxfp4_shuffle_b_sizes.argtypes = [i64, i64, ctypes.POINTER(i64), ctypes.POINTER(i64)]
+        lib.mxfp4_shuffle_b_sizes.restype = i32
+        lib.mxfp4_shuffle_b.argtypes = [vp, vp, i64, i64, vp, vp, vp]
+        lib.mxfp4_shuffle_b.restype = i32
+        lib.mxfp4_gemm_bshuffled.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, vp, vp]
+        lib.mxfp4_gemm_bshuffled.restype = i32
         _lib = lib
     return _lib
 
@@ -116,6 +123,22 @@ def mxfp4_gemm_swiglu(A_codes, A_scales, B_codes, B_scales, M, N, K, act_codes, 
                       act_bf16, stream):
     return int(load_library().mxfp4_gemm_swiglu(A_codes, A_scales, B_codes, B_scales, M, N, K,
                                                 act_codes, act_scales, act_bf16, stream))
+
+
+def mxfp4_shuffle_b_sizes(N, K):
+    """(rc, code_bytes, scale_bytes) of the pre-shuffled layout of B [N, K]."""
+    cb, sb = ctypes.c_int64(0), ctypes.c_int64(0)
+    rc = int(load_library().mxfp4_shuffle_b_sizes(N, K, ctypes.byref(cb), ctypes.byref(sb)))
+    return rc, cb.value, sb.value
+
+
+def mxfp4_shuffle_b(codes, scales, N, K, codes_sh, scales_sh, stream):
+    return int(load_library().mxfp4_shuffle_b(codes, scales, N, K, codes_sh, scales_sh, stream))
+
+
+def mxfp4_gemm_bshuffled(A_codes, A_scales, Bsh_codes, Bsh_scales, M, N, K, out_dtype, C, stream):
+    return int(load_library().mxfp4_gemm_bshuffled(A_codes, A_scales, Bsh_codes, Bsh_scales, M, N,
+                                                   K, out_dtype, C, stream))
 
 
 # ------------------------------------------------------- torch tensor layer
@@ -296,3 +319,52 @@ def gemm_swiglu(A_codes, A_scales, B_codes, B_scales, want_act=False, stream=Non
     if rc != 0:
         raise Mxfp4Error(rc, "mxfp4_gemm_swiglu")
     return (codes, scales, act) if want_act else (codes, scales)
+
+
+def shuffle_b(B_codes, B_scales, stream=None):
+    """Pre-shuffle an MXFP4 weight for gemm_bshuffled. Returns (codes_sh,
+    scales_sh) as flat uint8 device tensors in the library's block layout."""
+    import torch
+    N, Kh = B_codes.shape
+    K = 2 * Kh
+    _check(B_codes, "B_codes", torch.uint8, (N, K // 2))
+    _check(B_scales, "B_scales", torch.uint8, (N, K // 32))
+    rc, cb, sb = mxfp4_shuffle_b_sizes(N, K)
+    if rc != 0:
+        raise Mxfp4Error(rc, "mxfp4_shuffle_b_sizes")
+    dev = B_codes.device
+    codes_sh = torch.empty(cb, dtype=torch.uint8, device=dev)
+    scales_sh = torch.empty(sb, dtype=torch.uint8, device=dev)
+    rc = mxfp4_shuffle_b(B_codes.data_ptr(), B_scales.data_ptr(), N, K, codes_sh.data_ptr(),
+                         scales_sh.data_ptr(), _stream_handle(stream))
+    if rc != 0:
+        raise Mxfp4Error(rc, "mxfp4_shuffle_b")
+    return codes_sh, scales_sh
+
+
+def gemm_bshuffled(A_codes, A_scales, Bsh_codes, Bsh_scales, N, out_dtype=None, out=None,
+                   stream=None):
+    """gemm() with B pre-shuffled by shuffle_b (N: rows of B)."""
+    import torch
+    if out_dtype is None:
+        out_dtype = out.dtype if out is not None else torch.bfloat16
+    if out_dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("out_dtype must be torch.bfloat16 or torch.float32")
+    M, K = A_codes.shape[0], A_codes.shape[1] * 2
+    _check(A_codes, "A_codes", torch.uint8, (M, K // 2))
+    _check(A_scales, "A_scales", torch.uint8, (M, K // 32))
+    rc, cb, sb = mxfp4_shuffle_b_sizes(N, K)
+    if rc != 0:
+        raise Mxfp4Error(rc, "mxfp4_shuffle_b_sizes")
+    _check(Bsh_codes, "Bsh_codes", torch.uint8, (cb,))
+    _check(Bsh_scales, "Bsh_scales", torch.uint8, (sb,))
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=A_codes.device)
+    _check(out, "out", out_dtype, (M, N))
+    code = OUT_FP32 if out_dtype == torch.float32 else OUT_BF16
+    rc = mxfp4_gemm_bshuffled(A_codes.data_ptr(), A_scales.data_ptr(), Bsh_codes.data_ptr(),
+                              Bsh_scales.data_ptr(), M, N, K, code, out.data_ptr(),
+                              _stream_handle(stream))
+    if rc != 0:
+        raise Mxfp4Error(rc, "mxfp4_gemm_bshuffled")
+    return out

@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmxfp4.so")
 SOURCES = ["api.hip", "quantize.hip", "quantize_sr.hip", "quantize2d.hip", "gemm.hip",
-           "gemm_skinny.hip"]
+           "gemm_skinny.hip", "shuffle.hip"]
 ARCH = "gfx950"
 
 

@@ -161,6 +161,53 @@ int mxfp4_gemm(const void* A_codes, const void* A_scales, const void* B_codes,
                                           (int)K, fp32, C, st));
 }
 
+int mxfp4_shuffle_b_sizes(int64_t N, int64_t K, int64_t* code_bytes, int64_t* scale_bytes) {
+  if (!code_bytes || !scale_bytes) return MXFP4_EINVAL;
+  if (N < 1 || K < 256 || K % 256 != 0 || N > kMaxDim || K > kMaxGemmK) return MXFP4_EINVAL;
+  mxfp4::shuffled_b_sizes(N, K, code_bytes, scale_bytes);
+  if (*code_bytes >= kMaxBytes) return MXFP4_EINVAL;
+  return MXFP4_OK;
+}
+
+int mxfp4_shuffle_b(const void* codes, const void* scales, int64_t N, int64_t K, void* codes_sh,
+                    void* scales_sh, void* stream) {
+  if (!codes || !scales || !codes_sh || !scales_sh) return MXFP4_EINVAL;
+  int64_t cb = 0, sb = 0;
+  const int rc = mxfp4_shuffle_b_sizes(N, K, &cb, &sb);
+  if (rc != MXFP4_OK) return rc;
+  if (!aligned(codes, 16) || !aligned(codes_sh, 16) || !aligned(scales, 4) ||
+      !aligned(scales_sh, 4))
+    return MXFP4_EALIGN;
+  const int dev = check_device();
+  if (dev != MXFP4_OK) return dev;
+  return launch_status(mxfp4::launch_shuffle_b(codes, scales, (int)N, (int)K, codes_sh, scales_sh,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+int mxfp4_gemm_bshuffled(const void* A_codes, const void* A_scales, const void* Bsh_codes,
+                         const void* Bsh_scales, int64_t M, int64_t N, int64_t K, int out_dtype,
+                         void* C, void* stream) {
+  if (!A_codes || !A_scales || !Bsh_codes || !Bsh_scales || !C) return MXFP4_EINVAL;
+  if (M <= 0 || N <= 0 || K <= 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim)
+    return MXFP4_EINVAL;
+  if (K % 256 != 0 || M % 32 != 0 || N % 32 != 0 || K > kMaxGemmK) return MXFP4_EINVAL;
+  if (out_dtype != MXFP4_OUT_BF16 && out_dtype != MXFP4_OUT_FP32) return MXFP4_EINVAL;
+  const int64_t out_bytes = out_dtype == MXFP4_OUT_FP32 ? 4 : 2;
+  int64_t cb = 0, sb = 0;
+  mxfp4::shuffled_b_sizes(N, K, &cb, &sb);
+  if (M * (K / 2) >= kMaxBytes || cb >= kMaxBytes || M * N * out_bytes >= kMaxBytes)
+    return MXFP4_EINVAL;
+  if (!aligned(A_codes, 16) || !aligned(Bsh_codes, 16) || !aligned(A_scales, 4) ||
+      !aligned(Bsh_scales, 4) || !aligned(C, 16))
+    return MXFP4_EALIGN;
+  const int dev = check_device();
+  if (dev != MXFP4_OK) return dev;
+  return launch_status(mxfp4::launch_gemm_bshuffled(A_codes, A_scales, Bsh_codes, Bsh_scales,
+                                                    (int)M, (int)N, (int)K,
+                                                    out_dtype == MXFP4_OUT_FP32, C,
+                                                    static_cast<hipStream_t>(stream)));
+}
+
 int mxfp4_gemm_swiglu(const void* A_codes, const void* A_scales, const void* B_codes,
                       const void* B_scales, int64_t M, int64_t N, int64_t K, void* act_codes,
                       void* act_scales, void* act_bf16, void* stream) {

@@ -130,6 +130,9 @@ struct Ctx {
   int row_bytes, scale_row_bytes;
   int row0, col0, M, N;
   int Nh;                 // SwiGLU: activation columns (B rows per half)
+  int ksteps, nchunks;    // pre-shuffled B: K steps and 1024-K scale chunks
+  int b_scale_blk;        // pre-shuffled B: first scale block of this tile
+  uint32_t lane16;        // 16 * lane
   int klast, hlast;
   uint32_t code_lane[2];  // per-lane code DMA offset for row groups at 16 r, 16 r + 8
   const uint8_t* tile_a;  // wave-uniform code bases of this tile, less kDmaBias
@@ -208,11 +211,14 @@ __device__ __forceinline__ void load_a2(const Ctx& c, Tiles& t, int kt) {
       __builtin_amdgcn_readfirstlane(lds_addr(t.a[S]) + c.wave * 8192 + (Q0 / 4) * 4096);
   dma_pair<Q0>(c.tile_a + kt * kRowBytes, c.off_a[Q0], c.off_a[Q0 + 1], m0);
 }
-template <int Q0, int S>
+// A pre-shuffled B keeps each (tile, K step) as one 32 KiB block in LDS
+// order, so a K step advances the base by a block instead of a row chunk.
+template <bool kShufB, int Q0, int S>
 __device__ __forceinline__ void load_b2(const Ctx& c, Tiles& t, int kt) {
   const uint32_t m0 =
       __builtin_amdgcn_readfirstlane(lds_addr(t.b[S]) + c.wave * 8192 + (Q0 / 4) * 4096);
-  dma_pair<Q0>(c.tile_b + kt * kRowBytes, c.off_b[Q0], c.off_b[Q0 + 1], m0);
+  dma_pair<Q0>(c.tile_b + kt * (kShufB ? kTileBytes : kRowBytes), c.off_b[Q0], c.off_b[Q0 + 1],
+               m0);
 }
 
 // Scale part u (0..7) of operand X (0 = A, 1 = B) of chunk `chunk`: words
@@ -220,8 +226,19 @@ __device__ __forceinline__ void load_b2(const Ctx& c, Tiles& t, int kt) {
 // (lane / 4) % 8, r = 8 (u % 4) + 2 w + lane / 32, half = u / 4, so
 // row = 128 (u / 4) + 32 (lane % 4) + 8 (u % 4) + 2 w + lane / 32 and the
 // XOR key (r >> 1) & 7 = 4 (u % 2) + w.
-template <bool kGlu, int X, int U>
+template <bool kGlu, bool kShufB, int X, int U>
 __device__ __forceinline__ void load_scale_part(const Ctx& c, uint8_t* buf, int chunk) {
+  if constexpr (kShufB && X == 1) {
+    // The shuffled scale block is the LDS chunk image: part U of wave w is
+    // bytes 1024 U + 256 w + 4 lane of it.
+    const int chunk_c = min(chunk, c.nchunks - 1);
+    const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(buf) + kChunkBytes +
+                                                        4 * (256 * U + 64 * c.wave));
+    dma4(c.Bs + (int64_t)(c.b_scale_blk + chunk_c) * kChunkBytes + 1024 * U + 256 * c.wave +
+             (c.lane16 >> 2),
+         dst);
+    return;
+  }
   const uint8_t* base = X == 0 ? c.As : c.Bs;
   const int t_row = 128 * (U / 4) + 8 * (U % 4) + 2 * c.wave + c.scale_lane;
   const int row = X == 0 ? min(c.row0 + t_row, c.M - 1) : b_row<kGlu>(c, t_row);
@@ -238,16 +255,23 @@ __device__ __forceinline__ void load_scale_part(const Ctx& c, uint8_t* buf, int 
 // clamped base row. Only for chunks whose 8 half-steps all lie within K; the
 // last chunk of a K that is not a multiple of 1024 takes load_scale_part.
 constexpr int kScaleBias = 1024;
-template <bool kGlu, int X, int PP>
+template <bool kGlu, bool kShufB, int X, int PP>
 __device__ __forceinline__ void load_scale_pair(const Ctx& c, uint8_t* buf, int chunk) {
   const uint8_t* base = X == 0 ? c.As : c.Bs;
-  const int t_row = 128 * (PP / 2) + 16 * (PP % 2) + 2 * c.wave;
-  const int row_c = X == 0 ? min(c.row0 + t_row, c.M - 1) : b_row<kGlu>(c, t_row);
   // The last steps prefetch chunks past the end of K: those re-read the last
   // chunk (never used) instead of running past the scale rows.
   const int chunk_c = min(chunk, c.hlast / kChunk);
-  const uint8_t* sbase =
-      base + (int64_t)row_c * c.scale_row_bytes + kChunk * 4 * chunk_c - kScaleBias;
+  const uint8_t* sbase;
+  if constexpr (kShufB && X == 1) {
+    // Parts 2 PP, 2 PP + 1 of wave w: bytes 2048 PP + 256 w (+ 1024) of the
+    // shuffled block, the same offsets as in LDS.
+    sbase = base + (int64_t)(c.b_scale_blk + chunk_c) * kChunkBytes + 2048 * PP +
+            256 * c.wave - kScaleBias;
+  } else {
+    const int t_row = 128 * (PP / 2) + 16 * (PP % 2) + 2 * c.wave;
+    const int row_c = X == 0 ? min(c.row0 + t_row, c.M - 1) : b_row<kGlu>(c, t_row);
+    sbase = base + (int64_t)row_c * c.scale_row_bytes + kChunk * 4 * chunk_c - kScaleBias;
+  }
   const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr(buf) + X * kChunkBytes +
                                                      4 * (256 * (2 * PP) + 64 * c.wave));
   asm volatile(
@@ -259,13 +283,14 @@ __device__ __forceinline__ void load_scale_pair(const Ctx& c, uint8_t* buf, int 
 }
 
 // kFull: K is a multiple of 1024, so every chunk is whole.
-template <bool kFull, bool kGlu, int X, int PP>
+template <bool kFull, bool kGlu, bool kShufB, int X, int PP>
 __device__ __forceinline__ void load_scales2(const Ctx& c, uint8_t* buf, int chunk) {
-  if constexpr (kFull) {
-    load_scale_pair<kGlu, X, PP>(c, buf, chunk);
+  // Shuffled B scales are padded to whole chunks: always the pair form.
+  if constexpr (kFull || (kShufB && X == 1)) {
+    load_scale_pair<kGlu, kShufB, X, PP>(c, buf, chunk);
   } else {
-    load_scale_part<kGlu, X, 2 * PP>(c, buf, chunk);
-    load_scale_part<kGlu, X, 2 * PP + 1>(c, buf, chunk);
+    load_scale_part<kGlu, kShufB, X, 2 * PP>(c, buf, chunk);
+    load_scale_part<kGlu, kShufB, X, 2 * PP + 1>(c, buf, chunk);
   }
 }
 
@@ -320,7 +345,7 @@ __device__ __forceinline__ void step_barrier() {
 // T+1: A rows of loads 4..7 and all of B in phases 0-1 (A loads 0..3 came in
 // phase 3 of step T-1). Phase 3 issues step T+2's A loads 0..3 into `cur`
 // and scale parts 2P, 2P+1 of both operands for chunk (T+1)/4 + 1.
-template <bool kFull, bool kGlu, int P, int S>
+template <bool kFull, bool kGlu, bool kShufB, int P, int S>
 __device__ __forceinline__ void k_step(const Ctx& c0, Tiles& tl,
                                        uint8_t (*chunks)[2 * kChunkBytes], v16f_t (&acc)[4][4],
                                        Frags& fa, Frags& fb, HalfScales& sc0, HalfScales& sc1,
@@ -346,18 +371,18 @@ __device__ __forceinline__ void k_step(const Ctx& c0, Tiles& tl,
   mma_row<0, 2>(acc, fa, sc0);
   read_frag_a<S>(c, tl, 1, 0, fb.a[0]);
   read_frag_a<S>(c, tl, 1, 1, fb.a[1]);
-  load_b2<0, 1 - S>(c, tl, kb);
+  load_b2<kShufB, 0, 1 - S>(c, tl, kb);
   MXFP4_FENCE();
   mma_row<0, 3>(acc, fa, sc0);
   read_frag_a<S>(c, tl, 1, 2, fb.a[2]);
   read_frag_a<S>(c, tl, 1, 3, fb.a[3]);
-  load_b2<2, 1 - S>(c, tl, kb);
+  load_b2<kShufB, 2, 1 - S>(c, tl, kb);
   MXFP4_FENCE();
   // Phase 1: slice 1; read slice 2.
   mma_row<1, 0>(acc, fb, sc0);
   read_frag_b<S>(c, tl, 2, 0, fa.b[0]);
   read_frag_b<S>(c, tl, 2, 1, fa.b[1]);
-  load_b2<4, 1 - S>(c, tl, kb);
+  load_b2<kShufB, 4, 1 - S>(c, tl, kb);
   MXFP4_FENCE();
   mma_row<1, 1>(acc, fb, sc0);
   read_frag_b<S>(c, tl, 2, 2, fa.b[2]);
@@ -366,7 +391,7 @@ __device__ __forceinline__ void k_step(const Ctx& c0, Tiles& tl,
   mma_row<1, 2>(acc, fb, sc0);
   read_frag_a<S>(c, tl, 2, 0, fa.a[0]);
   read_frag_a<S>(c, tl, 2, 1, fa.a[1]);
-  load_b2<6, 1 - S>(c, tl, kb);
+  load_b2<kShufB, 6, 1 - S>(c, tl, kb);
   MXFP4_FENCE();
   mma_row<1, 3>(acc, fb, sc0);
   read_frag_a<S>(c, tl, 2, 2, fa.a[2]);
@@ -401,12 +426,12 @@ __device__ __forceinline__ void k_step(const Ctx& c0, Tiles& tl,
   read_frag_b<1 - S>(c, tl, 0, 0, fa.b[0]);
   read_frag_b<1 - S>(c, tl, 0, 1, fa.b[1]);
   load_a2<0, S>(c, tl, ka);
-  load_scales2<kFull, kGlu, 0, P>(c, pbuf, pchunk);
+  load_scales2<kFull, kGlu, kShufB, 0, P>(c, pbuf, pchunk);
   MXFP4_FENCE();
   mma_row<3, 1>(acc, fb, sc1);
   read_frag_b<1 - S>(c, tl, 0, 2, fa.b[2]);
   read_frag_b<1 - S>(c, tl, 0, 3, fa.b[3]);
-  load_scales2<kFull, kGlu, 1, P>(c, pbuf, pchunk);
+  load_scales2<kFull, kGlu, kShufB, 1, P>(c, pbuf, pchunk);
   MXFP4_FENCE();
   mma_row<3, 2>(acc, fb, sc1);
   read_frag_a<1 - S>(c, tl, 0, 0, fa.a[0]);
@@ -426,7 +451,7 @@ __device__ __forceinline__ void k_step(const Ctx& c0, Tiles& tl,
 
 // Issue the loads that start a tile: K step 0 and scale chunk 0 into slot 0
 // and chunks[0].
-template <bool kGlu>
+template <bool kGlu, bool kShufB>
 __device__ __forceinline__ void issue_tile_head(const Ctx& c0, Tiles& tl,
                                                 uint8_t (*chunks)[2 * kChunkBytes]) {
   Ctx c = c0;
@@ -435,46 +460,46 @@ __device__ __forceinline__ void issue_tile_head(const Ctx& c0, Tiles& tl,
   load_a2<2, 0>(c, tl, 0);
   load_a2<4, 0>(c, tl, 0);
   load_a2<6, 0>(c, tl, 0);
-  load_b2<0, 0>(c, tl, 0);
-  load_b2<2, 0>(c, tl, 0);
-  load_b2<4, 0>(c, tl, 0);
-  load_b2<6, 0>(c, tl, 0);
-  load_scale_part<kGlu, 0, 0>(c, chunks[0], 0);
-  load_scale_part<kGlu, 0, 1>(c, chunks[0], 0);
-  load_scale_part<kGlu, 0, 2>(c, chunks[0], 0);
-  load_scale_part<kGlu, 0, 3>(c, chunks[0], 0);
-  load_scale_part<kGlu, 0, 4>(c, chunks[0], 0);
-  load_scale_part<kGlu, 0, 5>(c, chunks[0], 0);
-  load_scale_part<kGlu, 0, 6>(c, chunks[0], 0);
-  load_scale_part<kGlu, 0, 7>(c, chunks[0], 0);
-  load_scale_part<kGlu, 1, 0>(c, chunks[0], 0);
-  load_scale_part<kGlu, 1, 1>(c, chunks[0], 0);
-  load_scale_part<kGlu, 1, 2>(c, chunks[0], 0);
-  load_scale_part<kGlu, 1, 3>(c, chunks[0], 0);
-  load_scale_part<kGlu, 1, 4>(c, chunks[0], 0);
-  load_scale_part<kGlu, 1, 5>(c, chunks[0], 0);
-  load_scale_part<kGlu, 1, 6>(c, chunks[0], 0);
-  load_scale_part<kGlu, 1, 7>(c, chunks[0], 0);
+  load_b2<kShufB, 0, 0>(c, tl, 0);
+  load_b2<kShufB, 2, 0>(c, tl, 0);
+  load_b2<kShufB, 4, 0>(c, tl, 0);
+  load_b2<kShufB, 6, 0>(c, tl, 0);
+  load_scale_part<kGlu, kShufB, 0, 0>(c, chunks[0], 0);
+  load_scale_part<kGlu, kShufB, 0, 1>(c, chunks[0], 0);
+  load_scale_part<kGlu, kShufB, 0, 2>(c, chunks[0], 0);
+  load_scale_part<kGlu, kShufB, 0, 3>(c, chunks[0], 0);
+  load_scale_part<kGlu, kShufB, 0, 4>(c, chunks[0], 0);
+  load_scale_part<kGlu, kShufB, 0, 5>(c, chunks[0], 0);
+  load_scale_part<kGlu, kShufB, 0, 6>(c, chunks[0], 0);
+  load_scale_part<kGlu, kShufB, 0, 7>(c, chunks[0], 0);
+  load_scale_part<kGlu, kShufB, 1, 0>(c, chunks[0], 0);
+  load_scale_part<kGlu, kShufB, 1, 1>(c, chunks[0], 0);
+  load_scale_part<kGlu, kShufB, 1, 2>(c, chunks[0], 0);
+  load_scale_part<kGlu, kShufB, 1, 3>(c, chunks[0], 0);
+  load_scale_part<kGlu, kShufB, 1, 4>(c, chunks[0], 0);
+  load_scale_part<kGlu, kShufB, 1, 5>(c, chunks[0], 0);
+  load_scale_part<kGlu, kShufB, 1, 6>(c, chunks[0], 0);
+  load_scale_part<kGlu, kShufB, 1, 7>(c, chunks[0], 0);
 }
 
 // What phase 3 of step "-1" would have issued: A loads 0..3 of step 1 and
 // parts 0, 1 of chunk 1. Exactly 8 loads: the tile's first wait is vmcnt(8).
-template <bool kGlu>
+template <bool kGlu, bool kShufB>
 __device__ __forceinline__ void issue_tile_tail(const Ctx& c0, Tiles& tl,
                                                 uint8_t (*chunks)[2 * kChunkBytes]) {
   Ctx c = c0;
   asm volatile("" : "+v"(c.scale_lane), "+v"(c.scale_t));
   load_a2<0, 1>(c, tl, min(1, c.klast));
   load_a2<2, 1>(c, tl, min(1, c.klast));
-  load_scale_part<kGlu, 0, 0>(c, chunks[1], 1);
-  load_scale_part<kGlu, 1, 0>(c, chunks[1], 1);
-  load_scale_part<kGlu, 0, 1>(c, chunks[1], 1);
-  load_scale_part<kGlu, 1, 1>(c, chunks[1], 1);
+  load_scale_part<kGlu, kShufB, 0, 0>(c, chunks[1], 1);
+  load_scale_part<kGlu, kShufB, 1, 0>(c, chunks[1], 1);
+  load_scale_part<kGlu, kShufB, 0, 1>(c, chunks[1], 1);
+  load_scale_part<kGlu, kShufB, 1, 1>(c, chunks[1], 1);
 }
 
 // Point the context at tile id p (XCD-aware order). A SwiGLU tile spans
 // 128 activation columns (256 B rows: 128 gate, 128 up).
-template <bool kGlu>
+template <bool kGlu, bool kShufB>
 __device__ __forceinline__ void set_tile(Ctx& c, int p, int tiles_m, int tiles_n) {
   int tm, tn;
   tile_of(p, tiles_m, tiles_n, tm, tn);
@@ -485,13 +510,21 @@ __device__ __forceinline__ void set_tile(Ctx& c, int p, int tiles_m, int tiles_n
   const int ra = min(c.row0 + 64 * c.wave, c.M - 8);
   const int rb = b_group_row<kGlu>(c, 64 * c.wave);
   c.tile_a = c.A + (int64_t)ra * c.row_bytes - kDmaBias;
-  c.tile_b = c.B + (int64_t)rb * c.row_bytes - kDmaBias;
+  if constexpr (kShufB) {
+    // Block (tile, step 0) of the shuffled B; this wave's rows start 8 KiB in.
+    c.tile_b = c.B + (int64_t)tn * c.ksteps * kTileBytes + 8192 * c.wave - kDmaBias;
+    c.b_scale_blk = tn * c.nchunks;
+  } else {
+    c.tile_b = c.B + (int64_t)rb * c.row_bytes - kDmaBias;
+  }
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
     const int ga = min(c.row0 + 64 * c.wave + 8 * q, c.M - 8) - ra;
     const int gb = b_group_row<kGlu>(c, 64 * c.wave + 8 * q) - rb;
     c.off_a[q] = (uint32_t)(ga * c.row_bytes) + c.code_lane[q & 1] + kDmaBias - (q % 4) * 1024;
-    c.off_b[q] = (uint32_t)(gb * c.row_bytes) + c.code_lane[q & 1] + kDmaBias - (q % 4) * 1024;
+    c.off_b[q] = kShufB ? c.lane16 + 4096 * (q / 4) + kDmaBias
+                        : (uint32_t)(gb * c.row_bytes) + c.code_lane[q & 1] + kDmaBias -
+                              (q % 4) * 1024;
   }
   // Scale pairs: part U = 2p + e of operand X reads tile row
   // 128 (U / 4) + 8 (U % 4) + 2 w + scale_lane (its global row clamped),
@@ -507,6 +540,10 @@ __device__ __forceinline__ void set_tile(Ctx& c, int p, int tiles_m, int tiles_n
       for (int e = 0; e < 2; ++e) {
         const int tr = tb + 8 * e + c.scale_lane;
         const int lane_row = (x == 0 ? min(c.row0 + tr, c.M - 1) : b_row<kGlu>(c, tr)) - row_c;
+        if (kShufB && x == 1) {
+          c.soff[x][pp][e] = (c.lane16 >> 2) + kScaleBias;
+          continue;
+        }
         const int t = c.scale_t ^ (4 * e + c.wave);
         c.soff[x][pp][e] =
             (uint32_t)(lane_row * c.scale_row_bytes + 4 * t + kScaleBias - 1024 * e);
@@ -698,7 +735,7 @@ __device__ __forceinline__ void store_tile_swiglu(const int row0, const int col0
   }
 }
 
-template <int kEpi, bool kFull>
+template <int kEpi, bool kFull, bool kShufB>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_tile_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ As,
                       const uint8_t* __restrict__ B, const uint8_t* __restrict__ Bs, int M, int N,
@@ -729,6 +766,9 @@ void gemm_tile_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__
   c.M = M;
   c.N = N;
   c.Nh = Nh;
+  c.ksteps = ksteps;
+  c.nchunks = (K + 1023) / 1024;
+  c.lane16 = 16u * (uint32_t)lane;
   c.klast = ksteps - 1;
   c.hlast = 2 * ksteps - 1;
   c.wave = wave;
@@ -757,9 +797,9 @@ void gemm_tile_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__
   // Persistent: this workgroup takes tiles blockIdx.x, + gridDim.x, ...; the
   // grid is a multiple of 8, so every tile id keeps its workgroup's XCD.
   int p = blockIdx.x;
-  set_tile<kGlu>(c, p, tiles_m, tiles_n);
-  issue_tile_head<kGlu>(c, tl, chunks);
-  issue_tile_tail<kGlu>(c, tl, chunks);
+  set_tile<kGlu, kShufB>(c, p, tiles_m, tiles_n);
+  issue_tile_head<kGlu, kShufB>(c, tl, chunks);
+  issue_tile_tail<kGlu, kShufB>(c, tl, chunks);
   for (; p < total; p += gridDim.x) {
     asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
 
@@ -779,14 +819,14 @@ void gemm_tile_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__
 
     int T = 0;
     for (; T + 4 <= ksteps; T += 4) {
-      k_step<kFull, kGlu, 1, 0>(c, tl, chunks, acc, fa, fb, sc0, sc1, T);
-      k_step<kFull, kGlu, 2, 1>(c, tl, chunks, acc, fa, fb, sc0, sc1, T + 1);
-      k_step<kFull, kGlu, 3, 0>(c, tl, chunks, acc, fa, fb, sc0, sc1, T + 2);
-      k_step<kFull, kGlu, 0, 1>(c, tl, chunks, acc, fa, fb, sc0, sc1, T + 3);
+      k_step<kFull, kGlu, kShufB, 1, 0>(c, tl, chunks, acc, fa, fb, sc0, sc1, T);
+      k_step<kFull, kGlu, kShufB, 2, 1>(c, tl, chunks, acc, fa, fb, sc0, sc1, T + 1);
+      k_step<kFull, kGlu, kShufB, 3, 0>(c, tl, chunks, acc, fa, fb, sc0, sc1, T + 2);
+      k_step<kFull, kGlu, kShufB, 0, 1>(c, tl, chunks, acc, fa, fb, sc0, sc1, T + 3);
     }
-    if (T < ksteps) k_step<kFull, kGlu, 1, 0>(c, tl, chunks, acc, fa, fb, sc0, sc1, T);
-    if (T + 1 < ksteps) k_step<kFull, kGlu, 2, 1>(c, tl, chunks, acc, fa, fb, sc0, sc1, T + 1);
-    if (T + 2 < ksteps) k_step<kFull, kGlu, 3, 0>(c, tl, chunks, acc, fa, fb, sc0, sc1, T + 2);
+    if (T < ksteps) k_step<kFull, kGlu, kShufB, 1, 0>(c, tl, chunks, acc, fa, fb, sc0, sc1, T);
+    if (T + 1 < ksteps) k_step<kFull, kGlu, kShufB, 2, 1>(c, tl, chunks, acc, fa, fb, sc0, sc1, T + 1);
+    if (T + 2 < ksteps) k_step<kFull, kGlu, kShufB, 3, 0>(c, tl, chunks, acc, fa, fb, sc0, sc1, T + 2);
     // Every load of this tile has landed and every LDS read has returned,
     // in all waves, before the next tile's loads reuse the buffers.
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -798,15 +838,15 @@ void gemm_tile_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__
       store_tile_swiglu(c.row0, c.col0, M, Nh, acc, wy, wx, lane, act_codes, act_scales,
                         static_cast<uint16_t*>(C));
       if (pn < total) {
-        set_tile<kGlu>(c, pn, tiles_m, tiles_n);
-        issue_tile_head<kGlu>(c, tl, chunks);
+        set_tile<kGlu, kShufB>(c, pn, tiles_m, tiles_n);
+        issue_tile_head<kGlu, kShufB>(c, tl, chunks);
       }
     } else if constexpr (kOutFp32) {
       // This epilogue does not touch LDS: the next tile's loads go first.
       const Ctx cur_tile = c;
       if (pn < total) {
-        set_tile<kGlu>(c, pn, tiles_m, tiles_n);
-        issue_tile_head<kGlu>(c, tl, chunks);
+        set_tile<kGlu, kShufB>(c, pn, tiles_m, tiles_n);
+        issue_tile_head<kGlu, kShufB>(c, tl, chunks);
       }
       store_tile<true>(cur_tile, acc, wy, wx, r, h, C);
     } else {
@@ -817,11 +857,11 @@ void gemm_tile_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__
       store_tile_bf16_lds(c, acc, wy, wx, lane, region, C);
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
       if (pn < total) {
-        set_tile<kGlu>(c, pn, tiles_m, tiles_n);
-        issue_tile_head<kGlu>(c, tl, chunks);
+        set_tile<kGlu, kShufB>(c, pn, tiles_m, tiles_n);
+        issue_tile_head<kGlu, kShufB>(c, tl, chunks);
       }
     }
-    if (pn < total) issue_tile_tail<kGlu>(c, tl, chunks);
+    if (pn < total) issue_tile_tail<kGlu, kShufB>(c, tl, chunks);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
@@ -858,17 +898,17 @@ static hipError_t persistent_workers(int& workers) {
   return hipSuccess;
 }
 
-template <int kEpi>
+template <int kEpi, bool kShufB = false>
 static void launch_tile_kernel(bool full, dim3 grid, hipStream_t stream, const uint8_t* a,
                                const uint8_t* as, const uint8_t* b, const uint8_t* bs, int M,
                                int N, int K, void* C, int tiles_m, int tiles_n,
                                uint8_t* act_codes, uint8_t* act_scales, int Nh) {
   if (full)
-    hipLaunchKernelGGL((gemm_tile_kernel<kEpi, true>), grid, dim3(kThreads), 0, stream, a, as, b,
-                       bs, M, N, K, C, tiles_m, tiles_n, act_codes, act_scales, Nh);
+    hipLaunchKernelGGL((gemm_tile_kernel<kEpi, true, kShufB>), grid, dim3(kThreads), 0, stream, a,
+                       as, b, bs, M, N, K, C, tiles_m, tiles_n, act_codes, act_scales, Nh);
   else
-    hipLaunchKernelGGL((gemm_tile_kernel<kEpi, false>), grid, dim3(kThreads), 0, stream, a, as, b,
-                       bs, M, N, K, C, tiles_m, tiles_n, act_codes, act_scales, Nh);
+    hipLaunchKernelGGL((gemm_tile_kernel<kEpi, false, kShufB>), grid, dim3(kThreads), 0, stream,
+                       a, as, b, bs, M, N, K, C, tiles_m, tiles_n, act_codes, act_scales, Nh);
 }
 
 hipError_t launch_gemm(const void* A, const void* As, const void* B, const void* Bs, int M, int N,
@@ -891,6 +931,29 @@ hipError_t launch_gemm(const void* A, const void* As, const void* B, const void*
   else
     launch_tile_kernel<kEpiBf16>(full, grid, stream, a, as, b, bs, M, N, K, C, tiles_m, tiles_n,
                                  nullptr, nullptr, 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_bshuffled(const void* A, const void* As, const void* Bsh, const void* Bssh,
+                                 int M, int N, int K, bool out_fp32, void* C, hipStream_t stream) {
+  int workers = 0;
+  hipError_t e = persistent_workers(workers);
+  if (e != hipSuccess) return e;
+  const int tiles_m = (M + kTileM - 1) / kTileM;
+  const int tiles_n = (N + kTileN - 1) / kTileN;
+  const int total = tiles_m * tiles_n;
+  const dim3 grid(total < workers ? total : workers);
+  const auto* a = static_cast<const uint8_t*>(A);
+  const auto* as = static_cast<const uint8_t*>(As);
+  const auto* b = static_cast<const uint8_t*>(Bsh);
+  const auto* bs = static_cast<const uint8_t*>(Bssh);
+  const bool full = K % 1024 == 0;
+  if (out_fp32)
+    launch_tile_kernel<kEpiFp32, true>(full, grid, stream, a, as, b, bs, M, N, K, C, tiles_m,
+                                       tiles_n, nullptr, nullptr, 0);
+  else
+    launch_tile_kernel<kEpiBf16, true>(full, grid, stream, a, as, b, bs, M, N, K, C, tiles_m,
+                                       tiles_n, nullptr, nullptr, 0);
   return hipGetLastError();
 }
 

@@ -36,6 +36,14 @@ hipError_t launch_gemm_swiglu(const void* A, const void* As, const void* B, cons
                               int N, int K, void* act_codes, void* act_scales, void* act_bf16,
                               hipStream_t stream);
 
+// Pre-shuffled weights: sizes of the shuffled codes and scales of B [N, K],
+// the shuffle itself, and the tile GEMM reading B in that layout.
+void shuffled_b_sizes(int64_t N, int64_t K, int64_t* code_bytes, int64_t* scale_bytes);
+hipError_t launch_shuffle_b(const void* codes, const void* scales, int N, int K, void* codes_sh,
+                            void* scales_sh, hipStream_t stream);
+hipError_t launch_gemm_bshuffled(const void* A, const void* As, const void* Bsh, const void* Bssh,
+                                 int M, int N, int K, bool out_fp32, void* C, hipStream_t stream);
+
 // Same contract, for M up to kSkinnyMaxM: one 32 x 32 tile of C per
 // workgroup, K split between its waves.
 constexpr int kSkinnyMaxM = 128;

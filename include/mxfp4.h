@@ -130,6 +130,34 @@ int mxfp4_gemm(const void* A_codes, const void* A_scales, const void* B_codes,
                const void* B_scales, int64_t M, int64_t N, int64_t K, int out_dtype,
                void* C, void* stream);
 
+/* Pre-shuffled weights. The a4w4 path of "Integrate MXFP4 hipblaslt GEMM
+ * support" (#697, Changes list) and the call reviewed on "Initial integration
+ * of a4w4 GEMM" (#663) take the weight pre-shuffled, with swizzled scales:
+ * re-arranged once so that the GEMM moves it without address arithmetic.
+ * The pages give no layout; this library's is the byte order in which its
+ * tile GEMM lands B in LDS:
+ *   codes: one 32 KiB block per (256-row tile nt, 256-K step ks) at
+ *     (nt * (K/256) + ks) * 32768; row x of the tile at x * 128, its
+ *     16-byte chunk p holding the row's chunk p ^ swz(x) of that step, with
+ *     swz(x) = (x & 6) | ((x ^ (x >> 3)) & 1);
+ *   scales: one 8 KiB block per (tile nt, 1024-K chunk ch) at
+ *     (nt * ceil(K/1024) + ch) * 8192; the 4-byte word (four scale bytes)
+ *     of row 128 h + 32 t + r and 128-K half-step s of the chunk at
+ *     128 (32 h + r) + 16 (s ^ ((r >> 1) & 7)) + 4 t;
+ *   rows past N and half-steps past K are zero.
+ * mxfp4_shuffle_b_sizes gives the two buffer sizes (N >= 1, K % 256 == 0,
+ * K <= 2^24). mxfp4_shuffle_b writes them from plain codes [N, K/2] and
+ * scales [N, K/32] (codes 16-byte aligned, scales 4-byte aligned, both
+ * outputs likewise); mxfp4_gemm_bshuffled is mxfp4_gemm with B given in
+ * this layout (same requirements, results equal up to fp32 summation order;
+ * it always runs the 256 x 256 tile kernel). Errors as mxfp4_gemm. */
+int mxfp4_shuffle_b_sizes(int64_t N, int64_t K, int64_t* code_bytes, int64_t* scale_bytes);
+int mxfp4_shuffle_b(const void* codes, const void* scales, int64_t N, int64_t K, void* codes_sh,
+                    void* scales_sh, void* stream);
+int mxfp4_gemm_bshuffled(const void* A_codes, const void* A_scales, const void* Bsh_codes,
+                         const void* Bsh_scales, int64_t M, int64_t N, int64_t K, int out_dtype,
+                         void* C, void* stream);
+
 /* Gate+up GEMM of a SwiGLU MLP with the activation fused into its epilogue
  * and requantized to MXFP4 for the down projection. B holds the stacked
  * weight [W_gate; W_up]: rows 0 .. N/2 - 1 are W_gate, rows N/2 .. N - 1

@@ -31,9 +31,10 @@ def _declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = mx.load_library()
     names = _declared_functions()
-    assert names == ["mxfp4_available", "mxfp4_gemm", "mxfp4_gemm_swiglu", "mxfp4_quantize",
-                     "mxfp4_quantize_2d", "mxfp4_quantize_2d_sr", "mxfp4_quantize_async",
-                     "mxfp4_quantize_sr", "mxfp4_strerror"]
+    assert names == ["mxfp4_available", "mxfp4_gemm", "mxfp4_gemm_bshuffled",
+                     "mxfp4_gemm_swiglu", "mxfp4_quantize", "mxfp4_quantize_2d",
+                     "mxfp4_quantize_2d_sr", "mxfp4_quantize_async", "mxfp4_quantize_sr",
+                     "mxfp4_shuffle_b", "mxfp4_shuffle_b_sizes", "mxfp4_strerror"]
     for n in names:
         assert hasattr(lib, n), n
 
@@ -81,6 +82,29 @@ def test_gemm_swiglu_rejects_nulls_and_misalignment():
         bad = list(args)
         bad[i] = P16 + off
         assert mx.mxfp4_gemm_swiglu(*bad) == EALIGN, i
+
+
+def test_shuffle_sizes_match_the_oracle_layout():
+    import oracle
+    for N, K in [(1, 256), (256, 256), (257, 1280), (8192, 8192), (6176, 7936)]:
+        rc, cb, sb = mx.mxfp4_shuffle_b_sizes(N, K)
+        assert rc == OK and (cb, sb) == oracle.shuffled_sizes(N, K)
+    for N, K in [(0, 256), (32, 128), (32, 300), (32, 0), (1 << 31, 256), (32, (1 << 24) + 256)]:
+        assert mx.mxfp4_shuffle_b_sizes(N, K)[0] == EINVAL
+
+
+def test_shuffle_and_shuffled_gemm_reject_bad_arguments():
+    assert mx.mxfp4_shuffle_b(None, P16, 32, 256, P16, P16, None) == EINVAL
+    assert mx.mxfp4_shuffle_b(P16, P16, 32, 300, P16, P16, None) == EINVAL
+    assert mx.mxfp4_shuffle_b(P16 + 8, P16, 32, 256, P16, P16, None) == EALIGN
+    assert mx.mxfp4_shuffle_b(P16, P16 + 2, 32, 256, P16, P16, None) == EALIGN
+    assert mx.mxfp4_shuffle_b(P16, P16, 32, 256, P16 + 8, P16, None) == EALIGN
+    for M, N, K in [(0, 32, 256), (33, 32, 256), (32, 48, 256), (32, 32, 128)]:
+        assert mx.mxfp4_gemm_bshuffled(P16, P16, P16, P16, M, N, K, mx.OUT_BF16, P16,
+                                       None) == EINVAL
+    assert mx.mxfp4_gemm_bshuffled(P16, P16, P16, P16, 32, 32, 256, 7, P16, None) == EINVAL
+    assert mx.mxfp4_gemm_bshuffled(P16, P16, P16 + 8, P16, 32, 32, 256, mx.OUT_BF16, P16,
+                                   None) == EALIGN
 
 
 def test_gemm_rejects_oversized_buffers():
@@ -159,6 +183,9 @@ def test_no_device_reports_unsupported():
     assert mx.mxfp4_quantize_sr(P16, 4, 32, 5, P16, P16, None) == EUNSUPPORTED
     assert mx.mxfp4_gemm_swiglu(P16, P16, P16, P16, 32, 256, 256, P16, P16, None,
                                 None) == EUNSUPPORTED
+    assert mx.mxfp4_shuffle_b(P16, P16, 32, 256, P16, P16, None) == EUNSUPPORTED
+    assert mx.mxfp4_gemm_bshuffled(P16, P16, P16, P16, 32, 32, 256, mx.OUT_BF16, P16,
+                                   None) == EUNSUPPORTED
     assert mx.mxfp4_quantize_2d_sr(P16, 32, 32, 5, P16, P16, P16, P16, None) == EUNSUPPORTED
 
 
