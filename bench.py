@@ -4,7 +4,9 @@ One step = row-wise BF16 -> MXFP4 quantize of the activation A [M, K] plus the
 block-scaled GEMM C = dq(A) dq(B)^T against pre-quantized weights B [N, K],
 on the square workload M = N = K = 8192 with BF16 output (the headline MXFP4
 GEMM shape). Inputs are seeded synthetic BF16 (N(0,1) with 1% of entries x100)
-resident in HBM before the timed region.
+resident in HBM before the timed region. Weight preparation (quantize, and
+for the tile kernel the one-time pre-shuffle of B) happens before it; the
+GEMM on B in its plain layout is timed alone beside it.
 
 Prints one JSON line:
   value        2*M*N*K / (time per step), TFLOP/s, whole step (quantize + GEMM)
@@ -212,6 +214,12 @@ def main():
     b_bytes = bc.numel() + bs.numel()
     copies = max(1, -(-2 * LLC_BYTES // b_bytes)) if hbm_bound else 1
     weights = [(bc, bs)] + [(bc.clone(), bs.clone()) for _ in range(copies - 1)]
+    # Larger GEMMs run on the tile kernel with B pre-shuffled once (part of
+    # the weight preparation, like its quantization); skinny ones (split-K
+    # kernel) take B as is.
+    shuffled = not hbm_bound
+    if shuffled:
+        bsh = mx.shuffle_b(bc, bs)
     ac = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
     as_ = torch.empty((M, K // 32), dtype=torch.uint8, device=dev)
     c = torch.empty((M, N), dtype=out_dtype, device=dev)
@@ -227,7 +235,10 @@ def main():
         mx.quantize(x, ac, as_)
         if ev is not None:
             ev[1].record(stream)
-        mx.gemm(ac, as_, wb, ws, out=c)
+        if shuffled:
+            mx.gemm_bshuffled(ac, as_, bsh[0], bsh[1], N, out=c)
+        else:
+            mx.gemm(ac, as_, wb, ws, out=c)
         if ev is not None:
             ev[2].record(stream)
 
@@ -275,13 +286,12 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / 20
 
-    # The same GEMM with B pre-shuffled once (mxfp4_shuffle_b), timed alone.
-    bsh_c, bsh_s = mx.shuffle_b(bc, bs)
-    gsh_ms = time_alone(lambda: mx.mxfp4_gemm_bshuffled(ac.data_ptr(), as_.data_ptr(),
-                                                        bsh_c.data_ptr(), bsh_s.data_ptr(), M, N,
-                                                        K, w.out_dtype, c.data_ptr(),
-                                                        stream.cuda_stream),
-                        "mxfp4_gemm_bshuffled")
+    # The GEMM on B in its plain layout, timed alone (the step's GEMM when
+    # the workload is skinny).
+    gplain_ms = time_alone(lambda: mx.mxfp4_gemm(ac.data_ptr(), as_.data_ptr(), bc.data_ptr(),
+                                                 bs.data_ptr(), M, N, K, w.out_dtype,
+                                                 c.data_ptr(), stream.cuda_stream),
+                           "mxfp4_gemm")
 
     seed = 0x5EED
     qsr_ms = time_alone(lambda: mx.mxfp4_quantize_sr(x.data_ptr(), M, K, seed, ac.data_ptr(),
@@ -332,7 +342,8 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": (f"{w.name}: quantize A[{M},{K}] BF16 -> MXFP4, then GEMM "
-                         f"{M}x{N}x{K} against pre-quantized B[{N},{K}], "
+                         f"{M}x{N}x{K} against pre-quantized"
+                         f"{', pre-shuffled' if shuffled else ''} B[{N},{K}], "
                          f"{'fp32' if w.out_dtype else 'bf16'} out"),
             "M": M, "N": N, "K": K,
             "out_dtype": "fp32" if w.out_dtype else "bf16",
@@ -342,8 +353,9 @@ def main():
         "quantize_gbps": quant_gbps,
         "quantize_ms": float(q_ms.mean()),
         "quantize_hbm_frac": quant_gbps / HBM_PEAK_GBPS,
-        "gemm_bshuffled_ms": gsh_ms,
-        "gemm_bshuffled_tflops": flops / (gsh_ms * 1e-3) / 1e12,
+        "gemm_b_layout": "pre-shuffled" if shuffled else "plain",
+        "gemm_plain_b_ms": gplain_ms,
+        "gemm_plain_b_tflops": flops / (gplain_ms * 1e-3) / 1e12,
         "quantize_sr_ms": qsr_ms,
         "quantize_sr_gbps": gbps(q_bytes, qsr_ms),
         "quantize_2d_ms": q2_ms,
