@@ -884,7 +884,7 @@ hipError_t init_kernels_for_current_device() {
   return hipSuccess;
 }
 
-static hipError_t persistent_workers(int& workers) {
+hipError_t device_workers(int& workers) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
@@ -914,7 +914,7 @@ static void launch_tile_kernel(bool full, dim3 grid, hipStream_t stream, const u
 hipError_t launch_gemm(const void* A, const void* As, const void* B, const void* Bs, int M, int N,
                        int K, bool out_fp32, void* C, hipStream_t stream) {
   int workers = 0;
-  hipError_t e = persistent_workers(workers);
+  hipError_t e = device_workers(workers);
   if (e != hipSuccess) return e;
   const int tiles_m = (M + kTileM - 1) / kTileM;
   const int tiles_n = (N + kTileN - 1) / kTileN;
@@ -937,7 +937,7 @@ hipError_t launch_gemm(const void* A, const void* As, const void* B, const void*
 hipError_t launch_gemm_bshuffled(const void* A, const void* As, const void* Bsh, const void* Bssh,
                                  int M, int N, int K, bool out_fp32, void* C, hipStream_t stream) {
   int workers = 0;
-  hipError_t e = persistent_workers(workers);
+  hipError_t e = device_workers(workers);
   if (e != hipSuccess) return e;
   const int tiles_m = (M + kTileM - 1) / kTileM;
   const int tiles_n = (N + kTileN - 1) / kTileN;
@@ -961,7 +961,7 @@ hipError_t launch_gemm_swiglu(const void* A, const void* As, const void* B, cons
                               int N, int K, void* act_codes, void* act_scales, void* act_bf16,
                               hipStream_t stream) {
   int workers = 0;
-  hipError_t e = persistent_workers(workers);
+  hipError_t e = device_workers(workers);
   if (e != hipSuccess) return e;
   const int Nh = N / 2;
   const int tiles_m = (M + kTileM - 1) / kTileM;

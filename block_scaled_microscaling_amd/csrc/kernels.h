@@ -53,4 +53,8 @@ hipError_t launch_gemm_skinny(const void* A, const void* As, const void* B, cons
 // One-time per-device set-up of kernel attributes (large LDS allocations).
 hipError_t init_kernels_for_current_device();
 
+// Workgroups of a one-per-CU persistent grid on the current device: the CU
+// count rounded down to a multiple of the XCD count (cached per device).
+hipError_t device_workers(int& workers);
+
 }  // namespace mxfp4
