@@ -225,3 +225,30 @@ def test_workload_full_size(name):
     misses = check_gemm_output(got, c_ref, s_ref)
     print(f"[gpu] {name}: {m_idx.size} sampled outputs, literal BF16 misses {misses}", flush=True)
     _assert_not_silent_zeros(got.float().cpu().numpy(), c_ref, s_ref)
+
+
+@pytest.mark.parametrize("M", [32, 256])
+def test_maximum_k_closed_form(M):
+    """K = 2^24, the largest K the GEMM accepts, on both kernels and on the
+    pre-shuffled path. A is all 1.0 (scale 127); row n of B holds 1.0 at
+    every k with k % 8192 == 2 n (2048 of them) under scale 127 + n % 3, so
+    C[m, n] = 2048 * 2^(n % 3) exactly: every K block of the range counts,
+    and any offset overflow along K would change the sums."""
+    K, N = 1 << 24, 64
+    announce(f"maximum K: M={M} N={N} K={K}")
+    a_codes = torch.full((M, K // 2), 0x22, dtype=torch.uint8, device=DEV)
+    a_scales = torch.full((M, K // 32), 127, dtype=torch.uint8, device=DEV)
+    b_codes = torch.zeros((N, K // 2), dtype=torch.uint8, device=DEV)
+    n = torch.arange(N, device=DEV)
+    cols = (4096 * torch.arange(K // 8192, device=DEV))[None, :] + n[:, None]   # byte of k = 2n + 8192 t
+    b_codes.scatter_(1, cols, 0x02)
+    b_scales = (127 + (n % 3)).to(torch.uint8)[:, None].expand(N, K // 32).contiguous()
+    want = (2048.0 * 2.0 ** (n % 3).float())[None, :].expand(M, N)
+    for dt in (torch.float32, torch.bfloat16):
+        got = mx.gemm(a_codes, a_scales, b_codes, b_scales, out_dtype=dt)
+        torch.cuda.synchronize()
+        assert torch.equal(got.float(), want), dt
+    bc, bs = mx.shuffle_b(b_codes, b_scales)
+    got = mx.gemm_bshuffled(a_codes, a_scales, bc, bs, N, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(got, want)
