@@ -53,6 +53,13 @@
 // Tile order. Tile ids are renumbered so that each XCD (every 8th workgroup)
 // walks a contiguous range of tiles, grouped 4 tile-rows at a time; the
 // tiles running together on one XCD then share A and B panels in its L2.
+// Variants (template parameters of gemm_tile_kernel):
+//   kEpi = kEpiSwiglu: the gate+up GEMM of a SwiGLU MLP with the activation
+//     and its MXFP4 requantize in the epilogue (store_tile_swiglu); B rows
+//     follow b_row's gate/up interleave.
+//   kShufB: B pre-shuffled by shuffle.hip into this kernel's LDS order, so
+//     every B DMA reads one contiguous 1 KiB piece of a 32 KiB block.
+//   kFull: K % 1024 == 0 (every scale chunk whole, no tail steps).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
