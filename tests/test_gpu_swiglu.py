@@ -53,6 +53,7 @@ def _check(ac, as_, bc, bs, rows=None):
 @pytest.mark.parametrize("M,N,K", [
     (256, 512, 256),      # one tile row, 2 activation tiles, K % 1024 != 0
     (64, 256, 1024),      # M < 256 (a partial tile row), one tile; K % 1024 == 0
+    (32, 512, 768),       # M = 32: one MFMA row block, the rest clamped
     (288, 768, 1280),     # ragged M, Nh = 384 (3 tiles), K % 1024 != 0
     (544, 1280, 2048),    # several tiles both ways, Nh = 640
 ])
