@@ -13,14 +13,14 @@ the down projection consumes act as its MXFP4 A operand. The MXFP4 GEMM
 contract of "Integrate MXFP4 hipblaslt GEMM support" (ROCm/TransformerEngine
 #697, Changes list) has no activation epilogue; fusing one is a widening of
 that GEMM, defined here as:
-  G1  g[m, j] = C[m, j], u[m, j] = C[m, Nh + j] for j < Nh, with C the MXFP4
+  W1  g[m, j] = C[m, j], u[m, j] = C[m, Nh + j] for j < Nh, with C the MXFP4
       GEMM of mxfp4_ref (float64 sum of dequantized products).
-  G2  act[m, j] = silu(g) * u, silu(z) = z / (1 + exp(-z)), float64.
-  G3  The kernel rounds its act to BF16 (nearest even) and quantizes those
+  W2  act[m, j] = silu(g) * u, silu(z) = z / (1 + exp(-z)), float64.
+  W3  The kernel rounds its act to BF16 (nearest even) and quantizes those
       BF16 values exactly as mxfp4_ref.quantize does (blocks of 32 along j).
-Readings (the pages are silent): the kernel evaluates G2 in fp32 from fp32
+Readings (the pages are silent): the kernel evaluates W2 in fp32 from fp32
 GEMM sums. Its act may differ from the float64 act by the GEMM tolerance
-propagated through G2 plus the fp32 evaluation error:
+propagated through W2 plus the fp32 evaluation error:
   tol = 1e-5 * (1.1 * S_g * |u| + |silu(g)| * S_u + 1.1e-5 * S_g * S_u)
         + 2**-16 * |act|
 where S_g, S_u are the sums of |products| of g and u (mxfp4_ref.gemm_block),
@@ -41,14 +41,14 @@ EVAL_REL_TOL = 2.0 ** -16
 
 
 def silu(z):
-    """G2: z * sigmoid(z) = z / (1 + exp(-z)) in float64 (exp overflow -> 0)."""
+    """W2: z * sigmoid(z) = z / (1 + exp(-z)) in float64 (exp overflow -> 0)."""
     z = np.asarray(z, dtype=np.float64)
     with np.errstate(over="ignore"):
         return z / (1.0 + np.exp(-z))
 
 
 def swiglu_reference(A_codes, A_scales, B_codes, B_scales, m_rows=None):
-    """G1, G2 for the rows m_rows of A (all if None).
+    """W1, W2 for the rows m_rows of A (all if None).
 
     B_codes [N, K/2] / B_scales [N, K/32] hold W_gate in rows 0..Nh-1 and
     W_up in rows Nh..N-1. Returns (act, tol), float64 [rows, Nh].

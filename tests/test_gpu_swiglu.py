@@ -1,6 +1,6 @@
 """GPU parity of the gate+up GEMM with the fused SwiGLU + MXFP4 requantize.
 
-Two checks per case, following readings G1-G3 of oracle/swiglu.py:
+Two checks per case, following readings W1-W3 of oracle/swiglu.py:
   * the BF16 activation the kernel quantized lies within the derived
     tolerance of the float64 act = silu(g) * u (oracle.swiglu_reference);
   * its codes and scales are bit-exact with the oracle's quantize of that

@@ -1,4 +1,4 @@
-"""Pins of the fused-SwiGLU oracle (oracle/swiglu.py, readings G1-G3).
+"""Pins of the fused-SwiGLU oracle (oracle/swiglu.py, readings W1-W3).
 
 silu is pinned against torch's float64 SiLU and closed forms; the gate/up
 split of the stacked weight against a GEMM whose outputs are known element
@@ -48,7 +48,7 @@ def _one_hot_b(Nh, K, pick):
 
 
 def test_gate_up_split_with_known_gemm_outputs():
-    """G1: with A's row holding the Q1 values and B one-hot, g[j] = x[j] and
+    """W1: with A's row holding the Q1 values and B one-hot, g[j] = x[j] and
     u[j] = x[Nh + j] exactly, so act[j] = silu(x[j]) * x[Nh + j]."""
     g = read_golden("q1_block.txt")
     vals = np.array([float(v) for v in g["input"]])             # 32 BF16-exact values
