@@ -599,12 +599,49 @@ __device__ __forceinline__ void store_tile(const Ctx& c, v16f_t (&acc)[4][4], in
 
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
-// BF16 epilogue through LDS: each wave parks its 128 x 128 BF16 block in a
-// 32 KiB region (256-byte rows; 16-byte chunk c of row x at c ^ (x % 16),
-// and its two 8-byte halves swapped when (x / 16) % 2 = 1, so both the
-// 8-byte writes of 32 rows and the 16-byte reads of one row are
-// conflict-free), then writes C with 16 lanes per 256-byte row: 4 rows, 8
-// whole cache lines per store instruction.
+// Read-back half of the BF16 epilogue: lane l copies rows x = 4 k + l / 16
+// (k = 0..15), 16-byte chunk l % 16, of a parked 64-row block to C. With
+// eight rows per iteration the swizzle key x % 16 = 4 (k % 4) + l / 16 and
+// the half swap (k / 4) % 2 are constants, so each read is one of four
+// per-lane bases plus an immediate. Rows at or past rows_left, and lanes
+// whose columns lie past N (n_ok false), store nothing.
+__device__ __forceinline__ void copy_parked_rows(const uint8_t* region, int lane, uint8_t* cptr,
+                                                 int64_t row4_bytes, bool n_ok, int rows_left) {
+  const int l4 = lane >> 4, cc = lane & 15;
+  const uint8_t* rb[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) rb[kk] = region + l4 * 256 + (((cc ^ l4) << 4) ^ (64 * kk));
+#pragma unroll 1
+  for (int g2 = 0; g2 < 2; ++g2) {
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      uint4 w[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        w[k] = *reinterpret_cast<const uint4*>(rb[k] + 1024 * (8 * g2 + 4 * e + k));
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int kr = 8 * g2 + 4 * e + k;
+        uint4 x = w[k];
+        if (e) x = make_uint4(x.z, x.w, x.x, x.y);
+        const u32x4_t o = {x.x, x.y, x.z, x.w};
+        // Whole lines, written once: stream them past L2 (8% faster when C
+        // is large, as in a 16384 x 28672 GEMM).
+        if (n_ok && 4 * kr + l4 < rows_left)
+          __builtin_nontemporal_store(o, reinterpret_cast<u32x4_t*>(cptr + kr * row4_bytes));
+      }
+    }
+  }
+}
+
+// BF16 epilogue through LDS, in two rounds of 64 rows (MFMA tile rows i =
+// 0, 1, then 2, 3): each wave parks a 64 x 128 BF16 block in a 16 KiB
+// region (256-byte rows; 16-byte chunk c of row x at c ^ (x % 16), and its
+// two 8-byte halves swapped when (x / 16) % 2 = 1, so both the 8-byte writes
+// of 32 rows and the 16-byte reads of one row are conflict-free), then
+// writes it to C with 16 lanes per 256-byte row: 4 rows, 8 whole cache
+// lines per store instruction. A wave whose block lies inside C issues
+// exactly 32 stores.
 __device__ __forceinline__ void store_tile_bf16_lds(const Ctx& c, v16f_t (&acc)[4][4], int wy,
                                                     int wx, int lane, uint8_t* region,
                                                     void* __restrict__ C) {
@@ -612,51 +649,36 @@ __device__ __forceinline__ void store_tile_bf16_lds(const Ctx& c, v16f_t (&acc)[
   asm volatile("" : "+v"(r), "+v"(h));
   const int swz = r & 15;
   const int half = 8 * (h ^ ((r >> 4) & 1));
+  const int mrow = c.row0 + wy * 128;  // first row and column of the wave's block
+  const int ncol = c.col0 + wx * 128;
+  const int l4 = lane >> 4, cc = lane & 15;
+  uint8_t* cptr = static_cast<uint8_t*>(C) + ((int64_t)(mrow + l4) * c.N + ncol + 8 * cc) * 2;
+  const int64_t row4_bytes = (int64_t)c.N * 8;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int rd = 0; rd < 2; ++rd) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      v16f_t v = acc[i][j];
-      asm volatile("" : "+v"(v));
+    for (int ii = 0; ii < 2; ++ii) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int off = (32 * i + r) * 256 + (((4 * j + q) ^ swz) << 4) + half;
-        *reinterpret_cast<uint2*>(region + off) =
-            make_uint2(pack_bf16x2(v[4 * q], v[4 * q + 1]), pack_bf16x2(v[4 * q + 2], v[4 * q + 3]));
+      for (int j = 0; j < 4; ++j) {
+        v16f_t v = acc[2 * rd + ii][j];
+        asm volatile("" : "+v"(v));
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int off = (32 * ii + r) * 256 + (((4 * j + q) ^ swz) << 4) + half;
+          *reinterpret_cast<uint2*>(region + off) = make_uint2(
+              pack_bf16x2(v[4 * q], v[4 * q + 1]), pack_bf16x2(v[4 * q + 2], v[4 * q + 3]));
+        }
+        MXFP4_FENCE();
       }
-      MXFP4_FENCE();
     }
-  }
-  const int cc = lane & 15;
-  const int n = c.col0 + wx * 128 + 8 * cc;
-  const bool n_ok = n < c.N;
-#pragma unroll 4
-  for (int k = 0; k < 32; ++k) {
-    const int x = 4 * k + (lane >> 4);
-    uint4 w = *reinterpret_cast<const uint4*>(region + x * 256 + ((cc ^ (x & 15)) << 4));
-    if ((x >> 4) & 1) w = make_uint4(w.z, w.w, w.x, w.y);
-    const int m = c.row0 + wy * 128 + x;
-    if (n_ok && m < c.M) {
-      // Whole lines, written once: stream them past L2 (8% faster when C is
-      // large, as in a 16384 x 28672 GEMM).
-      const u32x4_t o = {w.x, w.y, w.z, w.w};
-      __builtin_nontemporal_store(
-          o, reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(C) + (int64_t)m * c.N + n));
-    }
+    copy_parked_rows(region, lane, cptr + 16 * rd * row4_bytes, row4_bytes, ncol + 8 * cc < c.N,
+                     c.M - mrow - 64 * rd);
+    MXFP4_FENCE();
   }
 }
-
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float silu(float z) {
   return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
-}
-
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-
-// Two floats -> BF16 pair (round to nearest even) in one conversion.
-__device__ __forceinline__ uint32_t bf16x2_of(float lo, float hi) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
 }
 
 // SwiGLU + MXFP4 epilogue. Tiles (i, 2 b) and (i, 2 b + 1) of a wave hold
@@ -696,7 +718,7 @@ __device__ __forceinline__ void store_tile_swiglu(const int row0, const int col0
       }
       uint32_t w[8];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) w[k] = bf16x2_of(a[2 * k], a[2 * k + 1]);
+      for (int k = 0; k < 8; ++k) w[k] = pack_bf16x2(a[2 * k], a[2 * k + 1]);
       if (act != nullptr && ok) {
 #pragma unroll
         for (int q = 0; q < 4; ++q)
@@ -708,7 +730,7 @@ __device__ __forceinline__ void store_tile_swiglu(const int row0, const int col0
       const uint32_t mine = __float_as_uint(amax);
       const auto both = __builtin_amdgcn_permlane32_swap(mine, mine, false, false);
       const float bmax = fmaxf(__uint_as_float(both[0]), __uint_as_float(both[1]));
-      const uint32_t mx = bf16x2_of(bmax, 0.0f) & 0x7FFFu;
+      const uint32_t mx = pack_bf16x2(bmax, 0.0f) & 0x7FFFu;
       const uint32_t byte = (uint32_t)max((int)(mx >> 7) - 2, 0);
       const float scale = __uint_as_float(byte << 23);
       // d[0]: code bytes 4 q' + 2 h + {0, 1} for q' = 0, 1; d[1] for q' = 2, 3.
@@ -807,8 +829,17 @@ void gemm_tile_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__
   set_tile<kGlu, kShufB>(c, p, tiles_m, tiles_n);
   issue_tile_head<kGlu, kShufB>(c, tl, chunks);
   issue_tile_tail<kGlu, kShufB>(c, tl, chunks);
+  // BF16 C: this wave's previous block lay inside C, so its 32 stores went
+  // out between the head and the tail loads of this tile.
+  bool whole_prev = false;
   for (; p < total; p += gridDim.x) {
-    asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+    // Wait for the head loads (vector memory operations complete in issue
+    // order): outstanding may remain the 8 tail loads and, after a whole
+    // BF16 block, the 32 stores issued between head and tail.
+    if (kEpi == kEpiBf16 && whole_prev)
+      asm volatile("s_waitcnt vmcnt(40)\n\ts_barrier" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
 
     v16f_t acc[4][4];
 #pragma unroll
@@ -857,16 +888,19 @@ void gemm_tile_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__
       }
       store_tile<true>(cur_tile, acc, wy, wx, r, h, C);
     } else {
-      // Waves 0, 1 park their blocks in the A slots, waves 2, 3 in the B
-      // slots; the next tile's loads wait until every wave has read its
-      // block back.
-      uint8_t* region = wave < 2 ? tl.a[wave] : tl.b[wave - 2];
-      store_tile_bf16_lds(c, acc, wy, wx, lane, region, C);
-      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      // The next tile's head loads (slot 0, chunks[0]) go out before the C
+      // stores, so that they do not queue behind them; C is parked in slot 1
+      // (waves 0, 1 in A's, waves 2, 3 in B's, 16 KiB each), and the tail
+      // loads into slot 1 wait until every wave has read its block back.
+      const Ctx cur_tile = c;
+      whole_prev = cur_tile.row0 + wy * 128 + 128 <= M && cur_tile.col0 + wx * 128 + 128 <= N;
       if (pn < total) {
         set_tile<kGlu, kShufB>(c, pn, tiles_m, tiles_n);
         issue_tile_head<kGlu, kShufB>(c, tl, chunks);
       }
+      uint8_t* region = wave < 2 ? tl.a[1] + 16384 * wave : tl.b[1] + 16384 * (wave - 2);
+      store_tile_bf16_lds(cur_tile, acc, wy, wx, lane, region, C);
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     }
     if (pn < total) issue_tile_tail<kGlu, kShufB>(c, tl, chunks);
   }

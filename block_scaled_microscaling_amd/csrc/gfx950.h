@@ -24,11 +24,13 @@ __device__ __forceinline__ v16f_t mfma_fp4(const uint4& x, const uint4& y, v16f_
                                                          (int)sy);
 }
 
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Two floats -> a BF16 pair (round to nearest even, lo in the low half), one
+// v_cvt_pk_bf16_f32 (converting the halves one by one costs four VALU ops).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  const __bf16 l = (__bf16)lo;
-  const __bf16 h = (__bf16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, l) |
-         ((uint32_t)__builtin_bit_cast(uint16_t, h) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
 }
 
 // XOR swizzle of the 16-byte chunk index within a 128-byte LDS row: the
