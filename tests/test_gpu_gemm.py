@@ -128,6 +128,59 @@ def test_random_operands_many_tiles(M, N, K, out_dtype):
     _assert_not_silent_zeros(out.float().cpu().numpy(), c_ref, s_ref)
 
 
+def _tile_of(pid, tiles_m, tiles_n, n_xcd=8, group_m=4):
+    """The tile kernel's XCD-aware tile order (tile id -> tile row, column)."""
+    total = tiles_m * tiles_n
+    q, rem = divmod(total, n_xcd)
+    xcd, idx = pid % n_xcd, pid // n_xcd
+    p = xcd * q + min(xcd, rem) + idx
+    width = group_m * tiles_n
+    first_m = (p // width) * group_m
+    in_group = p - (p // width) * width
+    gsize = min(tiles_m - first_m, group_m)
+    return first_m + in_group % gsize, in_group // gsize
+
+
+def _edge_transitions(M, N, workers):
+    """(whole -> edge, edge -> whole) tile successions over the persistent
+    workgroups: a BF16 tile's C stores overlap the next tile's first loads
+    only after a tile that lies wholly inside C."""
+    tiles_m, tiles_n = -(-M // 256), -(-N // 256)
+    total = tiles_m * tiles_n
+    wp = pw = 0
+    for b in range(min(workers, total)):
+        prev = None
+        for p in range(b, total, workers):
+            tm, tn = _tile_of(p, tiles_m, tiles_n)
+            whole = 256 * tm + 256 <= M and 256 * tn + 256 <= N
+            if prev is not None:
+                wp += prev and not whole
+                pw += whole and not prev
+            prev = whole
+    return wp, pw
+
+
+@pytest.mark.parametrize("M,N,K", [(4384, 4128, 256), (4128, 4384, 1280)])
+def test_bf16_persistent_edge_tiles(M, N, K):
+    """More tiles than workgroups with ragged M and N, BF16 out: workgroups
+    run whole tiles followed by edge tiles (and the reverse), on plain and on
+    pre-shuffled B."""
+    workers = torch.cuda.get_device_properties(0).multi_processor_count // 8 * 8
+    wp, pw = _edge_transitions(M, N, workers)
+    announce(f"gemm bf16 {M}x{N}x{K}: {workers} workgroups, whole->edge {wp}, edge->whole {pw}")
+    assert wp > 0
+    Ac, Bc = random_codes(M, K, M + 7), random_codes(N, K, N + 8)
+    As, Bs = random_scales(M, K, K + 9), random_scales(N, K, K + 10)
+    A, As_d, B, Bs_d = (u8_to_dev(t) for t in (Ac, As, Bc, Bs))
+    plain = mx.gemm(A, As_d, B, Bs_d, out_dtype=torch.bfloat16)
+    bc, bs = mx.shuffle_b(B, Bs_d)
+    shuf = mx.gemm_bshuffled(A, As_d, bc, bs, N, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    c_ref, s_ref = oracle.gemm(Ac, As, Bc, Bs)
+    check_gemm_output(plain, c_ref, s_ref)
+    assert torch.equal(plain, shuf)
+
+
 @pytest.mark.parametrize("M", [96, 288])
 def test_wide_scale_range(M):
     """Scales 100..150 on both sides: products span 2^-54 .. 2^46."""
