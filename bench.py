@@ -15,12 +15,18 @@ Prints one JSON line:
                events recorded on the launch stream around every timed launch;
                for GEMMs with at most 128 rows of A (skinny) against HBM
                (8 TB/s): achieved = algorithmic bytes (A, B codes + scales,
-               C) / mean GEMM launch time, with B rotated through enough
-               copies that it is read from HBM each step
+               C) / mean time of back-to-back GEMM launches (one event pair
+               around them), with B rotated through enough copies that it
+               is read from HBM each launch
   cpu_baseline the float64 NumPy oracle on a bounded sample of the same
                workload (up to an 8192 x 8192 block of C over the full K, the
                whole square GEMM, including the oracle's quantize of the
                operand rows it needs)
+
+For skinny workloads a bounded spin kernel keeps the GPU busy for a few
+milliseconds before each timed region while the host queues the timed
+launches, so that the events time the GPU and not Python's launch rate (a
+skinny GEMM runs for less time than one launch takes the host).
 """
 
 import argparse
@@ -117,6 +123,27 @@ def cpu_baseline(a_bits, b_bits, K, rows=8192, cols=8192):
         "sample": (f"C block {rows}x{cols} over K={K}: oracle quantize of {rows}+{cols} rows, "
                    f"float64 dequantize, C and S matmuls; {dt:.2f} s wall"),
     }
+
+
+def make_holder(torch, stream):
+    """Return hold(ms): keep the GPU busy for about ms milliseconds with
+    torch's bounded spin kernel, so that the host queues the launches that
+    follow before the GPU reaches them. Events recorded between those
+    launches then time the GPU rather than the host's launch rate, which
+    decides the reading for kernels of a few microseconds."""
+    cycles = 1 << 22
+    torch.cuda._sleep(cycles)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    torch.cuda._sleep(cycles)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    per_ms = cycles / max(e0.elapsed_time(e1), 1e-3)
+
+    def hold(ms):
+        torch.cuda._sleep(int(per_ms * ms))
+    return hold
 
 
 def time_swiglu(mx, torch, dev, stream, reps=10):
@@ -249,8 +276,16 @@ def main():
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
+    # Skinny steps are shorter than the host's launch time: a spin before
+    # `start` lets the host queue them ahead of the GPU. Not for the large
+    # workloads: there the GPU is the slower side anyway, and an idle spin
+    # before MFMA-heavy work was measured to slow the next 50 steps by 12%
+    # while the clocks readjust.
+    hold = make_holder(torch, stream) if hbm_bound else (lambda ms: None)
+    hold_ms = 2.0 + 0.3 * args.steps if hbm_bound else 0.0
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
+    hold(hold_ms)
     start.record(stream)
     for i in range(args.steps):
         step(evs[i])
@@ -279,6 +314,7 @@ def main():
             once()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
+        hold(5.0)
         e0.record(stream)
         for _ in range(20):
             once()
@@ -315,13 +351,40 @@ def main():
     def gbps(nbytes, ms):
         return None if ms is None else nbytes / (ms * 1e-3) / 1e9
 
+    # Skinny GEMM launch time: the per-launch events of the steps add their
+    # own few microseconds to a kernel of about ten, so the roofline takes
+    # the mean of back-to-back launches on the rotated B copies (one event
+    # pair around them).
+    g_rot_ms = None
+    if hbm_bound:
+        reps = 10 * copies
+
+        def gemm_rot(i):
+            wb, ws = weights[i % copies]
+            rc = mx.mxfp4_gemm(ac.data_ptr(), as_.data_ptr(), wb.data_ptr(), ws.data_ptr(), M, N,
+                               K, w.out_dtype, c.data_ptr(), stream.cuda_stream)
+            if rc != 0:
+                raise mx.Mxfp4Error(rc, "mxfp4_gemm")
+        for i in range(copies):
+            gemm_rot(i)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        hold(5.0)
+        e0.record(stream)
+        for i in range(reps):
+            gemm_rot(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        g_rot_ms = e0.elapsed_time(e1) / reps
+
     traffic = read_traffic(args.traffic_json, w.name)
     out_bytes = 4 if w.out_dtype == mx.OUT_FP32 else 2
     gemm_bytes = (M + N) * (K // 2 + K // 32) + M * N * out_bytes
     gemm_gbps = gemm_bytes / (g_ms.mean() * 1e-3) / 1e9
     if hbm_bound:
-        roofline = {"bound": "hbm", "achieved": gemm_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                    "frac": gemm_gbps / HBM_PEAK_GBPS, "traffic": traffic}
+        rot_gbps = gemm_bytes / (g_rot_ms * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": rot_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                    "frac": rot_gbps / HBM_PEAK_GBPS, "traffic": traffic}
     else:
         roofline = {"bound": "mfma", "achieved": gemm_tflops, "peak": FP4_DENSE_PEAK_TFLOPS,
                     "unit": "TFLOP/s", "frac": gemm_tflops / FP4_DENSE_PEAK_TFLOPS,
@@ -363,7 +426,9 @@ def main():
         "quantize_2d_sr_ms": q2sr_ms,
         "quantize_2d_sr_gbps": gbps(q2_bytes, q2sr_ms),
         "wall_s_timed": t_wall,
+        "gpu_hold_ms_before_timed": hold_ms,
         "gemm_gbps_algorithmic": gemm_gbps,
+        "gemm_rotated_back_to_back_ms": g_rot_ms,
         "b_copies_rotated": copies,
         "roofline": roofline,
     }

@@ -47,8 +47,10 @@
 //     of its 4 tiles; a byte permute then picks the lane half's K blocks and
 //     the MFMA's op_sel picks the byte. The half-step index is XOR-swizzled
 //     by the row so that these reads are conflict-free too.
-// Epilogue. BF16 output is parked in LDS and written with whole cache lines
-// per store instruction; FP32 output is stored straight from the
+// Epilogue. The next tile's first loads are issued before C is written, so
+// that they do not queue behind its stores. BF16 output is parked in the
+// second K-step slot (two rounds of 64 rows) and written with whole cache
+// lines per store instruction; FP32 output is stored straight from the
 // accumulators (16 bytes per lane).
 // Tile order. Tile ids are renumbered so that each XCD (every 8th workgroup)
 // walks a contiguous range of tiles, grouped 4 tile-rows at a time; the
