@@ -11,13 +11,15 @@ GEMM on B in its plain layout is timed alone beside it.
 Prints one JSON line:
   value        2*M*N*K / (time per step), TFLOP/s, whole step (quantize + GEMM)
   roofline     the GEMM kernel against the FP4 MFMA dense peak (10.1 PFLOP/s):
-               achieved = 2*M*N*K / mean GEMM launch time, measured with HIP
-               events recorded on the launch stream around every timed launch;
-               for GEMMs with at most 128 rows of A (skinny) against HBM
-               (8 TB/s): achieved = algorithmic bytes (A, B codes + scales,
-               C) / mean time of back-to-back GEMM launches (one event pair
-               around them), with B rotated through enough copies that it
-               is read from HBM each launch
+               achieved = 2*M*N*K / mean GEMM launch time; for GEMMs with at
+               most 128 rows of A (skinny) against HBM (8 TB/s): achieved =
+               algorithmic bytes (A, B codes + scales, C) / mean launch time,
+               with B rotated through enough copies that it is read from HBM
+               each launch. Launch times come from back-to-back launches on
+               the launch stream with one HIP event pair around them (events
+               between launches add a few microseconds to each); so does
+               every other per-kernel time in the line. The timed steps have
+               no events inside.
   cpu_baseline the float64 NumPy oracle on a bounded sample of the same
                workload (up to an 8192 x 8192 block of C over the full K, the
                whole square GEMM, including the oracle's quantize of the
@@ -254,26 +256,22 @@ def main():
 
     counter = [0]
 
-    def step(ev=None):
-        wb, ws = weights[counter[0] % copies]
-        counter[0] += 1
-        if ev is not None:
-            ev[0].record(stream)
-        mx.quantize(x, ac, as_)
-        if ev is not None:
-            ev[1].record(stream)
+    def gemm_step(i):
+        wb, ws = weights[i % copies]
         if shuffled:
             mx.gemm_bshuffled(ac, as_, bsh[0], bsh[1], N, out=c)
         else:
             mx.gemm(ac, as_, wb, ws, out=c)
-        if ev is not None:
-            ev[2].record(stream)
+
+    def step():
+        mx.quantize(x, ac, as_)
+        gemm_step(counter[0])
+        counter[0] += 1
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     # Skinny steps are shorter than the host's launch time: a spin before
@@ -286,51 +284,56 @@ def main():
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
     hold(hold_ms)
+    # Nothing but the steps between the two events: events recorded between
+    # launches add a few microseconds of their own to each.
     start.record(stream)
-    for i in range(args.steps):
-        step(evs[i])
+    for _ in range(args.steps):
+        step()
     stop.record(stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
 
     ms_total = start.elapsed_time(stop)
     ms_step = ms_total / args.steps
-    q_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
-    g_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
     flops = 2.0 * M * N * K
-    gemm_tflops = flops / (g_ms.mean() * 1e-3) / 1e12
     q_bytes = M * K * 2 + M * K // 2 + M * K // 32
-    quant_gbps = q_bytes / (q_ms.mean() * 1e-3) / 1e9
 
-    # Widenings of the quantize step, each timed alone on the same
-    # activation (20 back-to-back launches after 3 untimed ones): stochastic
-    # rounding, and the bidimensional (rowwise + columnwise) forms.
-    def time_alone(launch, name):
-        def once():
-            rc = launch()
-            if rc != 0:
+    # Launch times of the step's kernels and of the widenings, each over
+    # back-to-back launches on the launch stream (3 untimed, then `reps`
+    # between one event pair).
+    def time_alone(launch, name, reps=20):
+        def once(i):
+            rc = launch(i)  # a C status from the raw entries; the helpers raise
+            if isinstance(rc, int) and rc != 0:
                 raise mx.Mxfp4Error(rc, name)
-        for _ in range(3):
-            once()
+        for i in range(3):
+            once(i)
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         hold(5.0)
         e0.record(stream)
-        for _ in range(20):
-            once()
+        for i in range(reps):
+            once(i)
         e1.record(stream)
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / 20
+        return e0.elapsed_time(e1) / reps
+
+    # The step's GEMM (skinny: B rotated through its copies, so each launch
+    # reads B from HBM) and the step's quantize.
+    g_ms = time_alone(gemm_step, "gemm", reps=10 * copies if hbm_bound else 20)
+    q_ms = time_alone(lambda i: mx.quantize(x, ac, as_), "quantize")
+    gemm_tflops = flops / (g_ms * 1e-3) / 1e12
+    quant_gbps = q_bytes / (q_ms * 1e-3) / 1e9
 
     # The GEMM on B in its plain layout, timed alone (the step's GEMM when
     # the workload is skinny).
-    gplain_ms = time_alone(lambda: mx.mxfp4_gemm(ac.data_ptr(), as_.data_ptr(), bc.data_ptr(),
+    gplain_ms = time_alone(lambda i: mx.mxfp4_gemm(ac.data_ptr(), as_.data_ptr(), bc.data_ptr(),
                                                  bs.data_ptr(), M, N, K, w.out_dtype,
                                                  c.data_ptr(), stream.cuda_stream),
                            "mxfp4_gemm")
 
     seed = 0x5EED
-    qsr_ms = time_alone(lambda: mx.mxfp4_quantize_sr(x.data_ptr(), M, K, seed, ac.data_ptr(),
+    qsr_ms = time_alone(lambda i: mx.mxfp4_quantize_sr(x.data_ptr(), M, K, seed, ac.data_ptr(),
                                                      as_.data_ptr(), stream.cuda_stream),
                         "mxfp4_quantize_sr")
     q2_out = (torch.empty((M, K // 2), dtype=torch.uint8, device=dev),
@@ -340,10 +343,10 @@ def main():
     q2_ms = q2sr_ms = None
     if M % 32 == 0:
         ptrs = [t.data_ptr() for t in q2_out]
-        q2_ms = time_alone(lambda: mx.mxfp4_quantize_2d(x.data_ptr(), M, K, *ptrs,
+        q2_ms = time_alone(lambda i: mx.mxfp4_quantize_2d(x.data_ptr(), M, K, *ptrs,
                                                         stream.cuda_stream),
                            "mxfp4_quantize_2d")
-        q2sr_ms = time_alone(lambda: mx.mxfp4_quantize_2d_sr(x.data_ptr(), M, K, seed, *ptrs,
+        q2sr_ms = time_alone(lambda i: mx.mxfp4_quantize_2d_sr(x.data_ptr(), M, K, seed, *ptrs,
                                                              stream.cuda_stream),
                              "mxfp4_quantize_2d_sr")
     q2_bytes = 2 * M * K + 2 * (M * K // 2 + M * K // 32)
@@ -351,40 +354,13 @@ def main():
     def gbps(nbytes, ms):
         return None if ms is None else nbytes / (ms * 1e-3) / 1e9
 
-    # Skinny GEMM launch time: the per-launch events of the steps add their
-    # own few microseconds to a kernel of about ten, so the roofline takes
-    # the mean of back-to-back launches on the rotated B copies (one event
-    # pair around them).
-    g_rot_ms = None
-    if hbm_bound:
-        reps = 10 * copies
-
-        def gemm_rot(i):
-            wb, ws = weights[i % copies]
-            rc = mx.mxfp4_gemm(ac.data_ptr(), as_.data_ptr(), wb.data_ptr(), ws.data_ptr(), M, N,
-                               K, w.out_dtype, c.data_ptr(), stream.cuda_stream)
-            if rc != 0:
-                raise mx.Mxfp4Error(rc, "mxfp4_gemm")
-        for i in range(copies):
-            gemm_rot(i)
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        hold(5.0)
-        e0.record(stream)
-        for i in range(reps):
-            gemm_rot(i)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        g_rot_ms = e0.elapsed_time(e1) / reps
-
     traffic = read_traffic(args.traffic_json, w.name)
     out_bytes = 4 if w.out_dtype == mx.OUT_FP32 else 2
     gemm_bytes = (M + N) * (K // 2 + K // 32) + M * N * out_bytes
-    gemm_gbps = gemm_bytes / (g_ms.mean() * 1e-3) / 1e9
+    gemm_gbps = gemm_bytes / (g_ms * 1e-3) / 1e9
     if hbm_bound:
-        rot_gbps = gemm_bytes / (g_rot_ms * 1e-3) / 1e9
-        roofline = {"bound": "hbm", "achieved": rot_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                    "frac": rot_gbps / HBM_PEAK_GBPS, "traffic": traffic}
+        roofline = {"bound": "hbm", "achieved": gemm_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                    "frac": gemm_gbps / HBM_PEAK_GBPS, "traffic": traffic}
     else:
         roofline = {"bound": "mfma", "achieved": gemm_tflops, "peak": FP4_DENSE_PEAK_TFLOPS,
                     "unit": "TFLOP/s", "frac": gemm_tflops / FP4_DENSE_PEAK_TFLOPS,
@@ -412,9 +388,9 @@ def main():
             "out_dtype": "fp32" if w.out_dtype else "bf16",
         },
         "gemm_tflops": gemm_tflops,
-        "gemm_ms": float(g_ms.mean()),
+        "gemm_ms": g_ms,
         "quantize_gbps": quant_gbps,
-        "quantize_ms": float(q_ms.mean()),
+        "quantize_ms": q_ms,
         "quantize_hbm_frac": quant_gbps / HBM_PEAK_GBPS,
         "gemm_b_layout": "pre-shuffled" if shuffled else "plain",
         "gemm_plain_b_ms": gplain_ms,
@@ -428,7 +404,6 @@ def main():
         "wall_s_timed": t_wall,
         "gpu_hold_ms_before_timed": hold_ms,
         "gemm_gbps_algorithmic": gemm_gbps,
-        "gemm_rotated_back_to_back_ms": g_rot_ms,
         "b_copies_rotated": copies,
         "roofline": roofline,
     }
