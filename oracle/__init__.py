@@ -40,6 +40,10 @@ from .shuffle import (  # noqa: F401
     shuffle_b,
     unshuffle_b,
 )
+from .frag import (  # noqa: F401
+    to_frag,
+    from_frag,
+)
 from .compare import (  # noqa: F401
     FP32_REL_TOL,
     round_to_bf16,
