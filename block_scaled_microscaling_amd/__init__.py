@@ -7,8 +7,9 @@ marshals arguments. PyTorch supplies device memory and streams.
 Two layers, same names as the C ABI:
   * mxfp4_available, mxfp4_strerror, mxfp4_quantize, mxfp4_quantize_async,
     mxfp4_quantize_2d, mxfp4_quantize_sr, mxfp4_quantize_2d_sr, mxfp4_gemm,
-    mxfp4_gemm_swiglu take raw device pointers (ints) and return the C
-    status code.
+    mxfp4_gemm_swiglu, mxfp4_shuffle_b(_sizes), mxfp4_gemm_bshuffled,
+    mxfp4_quantize_frag, mxfp4_to_frag, mxfp4_gemm_frag take raw device
+    pointers (ints) and return the C status code.
   * quantize(x), quantize_2d(x), quantize_sr(x, seed), quantize_2d_sr(x,
     seed), gemm(...) and gemm_swiglu(...) take torch tensors, check their dtype, device,
     shape and contiguity, allocate outputs when none are given, enqueue on
@@ -26,7 +27,8 @@ __all__ = [
     "mxfp4_quantize_2d", "mxfp4_quantize_sr", "mxfp4_quantize_2d_sr", "mxfp4_gemm",
     "mxfp4_gemm_swiglu", "quantize", "quantize_2d", "quantize_sr", "quantize_2d_sr", "gemm",
     "gemm_swiglu", "mxfp4_shuffle_b_sizes", "mxfp4_shuffle_b", "mxfp4_gemm_bshuffled",
-    "shuffle_b", "gemm_bshuffled",
+    "shuffle_b", "gemm_bshuffled", "mxfp4_quantize_frag", "mxfp4_to_frag", "mxfp4_gemm_frag",
+    "quantize_frag", "to_frag", "gemm_frag",
 ]
 
 OUT_BF16 = 0
@@ -77,6 +79,12 @@ def load_library():
         lib.mxfp4_shuffle_b.restype = i32
         lib.mxfp4_gemm_bshuffled.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, vp, vp]
         lib.mxfp4_gemm_bshuffled.restype = i32
+        lib.mxfp4_quantize_frag.argtypes = [vp, i64, i64, vp, vp, vp]
+        lib.mxfp4_quantize_frag.restype = i32
+        lib.mxfp4_to_frag.argtypes = [vp, vp, i64, i64, vp, vp, vp]
+        lib.mxfp4_to_frag.restype = i32
+        lib.mxfp4_gemm_frag.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, vp, vp]
+        lib.mxfp4_gemm_frag.restype = i32
         _lib = lib
     return _lib
 
@@ -139,6 +147,19 @@ def mxfp4_shuffle_b(codes, scales, N, K, codes_sh, scales_sh, stream):
 def mxfp4_gemm_bshuffled(A_codes, A_scales, Bsh_codes, Bsh_scales, M, N, K, out_dtype, C, stream):
     return int(load_library().mxfp4_gemm_bshuffled(A_codes, A_scales, Bsh_codes, Bsh_scales, M, N,
                                                    K, out_dtype, C, stream))
+
+
+def mxfp4_quantize_frag(x_bf16, M, K, codes_frag, scales_frag, stream):
+    return int(load_library().mxfp4_quantize_frag(x_bf16, M, K, codes_frag, scales_frag, stream))
+
+
+def mxfp4_to_frag(codes, scales, R, K, codes_frag, scales_frag, stream):
+    return int(load_library().mxfp4_to_frag(codes, scales, R, K, codes_frag, scales_frag, stream))
+
+
+def mxfp4_gemm_frag(A_frag, A_scales_frag, B_frag, B_scales_frag, M, N, K, out_dtype, C, stream):
+    return int(load_library().mxfp4_gemm_frag(A_frag, A_scales_frag, B_frag, B_scales_frag, M, N,
+                                              K, out_dtype, C, stream))
 
 
 # ------------------------------------------------------- torch tensor layer
@@ -367,4 +388,67 @@ def gemm_bshuffled(A_codes, A_scales, Bsh_codes, Bsh_scales, N, out_dtype=None, 
                               _stream_handle(stream))
     if rc != 0:
         raise Mxfp4Error(rc, "mxfp4_gemm_bshuffled")
+    return out
+
+
+def quantize_frag(x, codes=None, scales=None, stream=None):
+    """Row-wise BF16 -> MXFP4 written in fragment order. x: bfloat16 [M, K]
+    (M % 32 == 0, K % 256 == 0). Returns flat uint8 (codes [M*K/2], scales
+    [M*K/32])."""
+    import torch
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [M, K]")
+    M, K = x.shape
+    _check(x, "x", torch.bfloat16, (M, K))
+    if codes is None:
+        codes = torch.empty(M * K // 2, dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(M * K // 32, dtype=torch.uint8, device=x.device)
+    _check(codes, "codes", torch.uint8, (M * K // 2,))
+    _check(scales, "scales", torch.uint8, (M * K // 32,))
+    rc = mxfp4_quantize_frag(x.data_ptr(), M, K, codes.data_ptr(), scales.data_ptr(),
+                             _stream_handle(stream))
+    if rc != 0:
+        raise Mxfp4Error(rc, "mxfp4_quantize_frag")
+    return codes, scales
+
+
+def to_frag(codes, scales, stream=None):
+    """Plain MXFP4 codes [R, K/2] and scales [R, K/32] -> fragment order (flat
+    uint8 codes [R*K/2], scales [R*K/32])."""
+    import torch
+    R, Kh = codes.shape
+    K = 2 * Kh
+    _check(codes, "codes", torch.uint8, (R, K // 2))
+    _check(scales, "scales", torch.uint8, (R, K // 32))
+    cf = torch.empty(R * K // 2, dtype=torch.uint8, device=codes.device)
+    sf = torch.empty(R * K // 32, dtype=torch.uint8, device=codes.device)
+    rc = mxfp4_to_frag(codes.data_ptr(), scales.data_ptr(), R, K, cf.data_ptr(), sf.data_ptr(),
+                       _stream_handle(stream))
+    if rc != 0:
+        raise Mxfp4Error(rc, "mxfp4_to_frag")
+    return cf, sf
+
+
+def gemm_frag(A_frag, A_scales_frag, B_frag, B_scales_frag, M, N, K, out_dtype=None, out=None,
+              stream=None):
+    """gemm() with both operands in fragment order (flat uint8 tensors)."""
+    import torch
+    if out_dtype is None:
+        out_dtype = out.dtype if out is not None else torch.bfloat16
+    if out_dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("out_dtype must be torch.bfloat16 or torch.float32")
+    _check(A_frag, "A_frag", torch.uint8, (M * K // 2,))
+    _check(A_scales_frag, "A_scales_frag", torch.uint8, (M * K // 32,))
+    _check(B_frag, "B_frag", torch.uint8, (N * K // 2,))
+    _check(B_scales_frag, "B_scales_frag", torch.uint8, (N * K // 32,))
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=A_frag.device)
+    _check(out, "out", out_dtype, (M, N))
+    code = OUT_FP32 if out_dtype == torch.float32 else OUT_BF16
+    rc = mxfp4_gemm_frag(A_frag.data_ptr(), A_scales_frag.data_ptr(), B_frag.data_ptr(),
+                         B_scales_frag.data_ptr(), M, N, K, code, out.data_ptr(),
+                         _stream_handle(stream))
+    if rc != 0:
+        raise Mxfp4Error(rc, "mxfp4_gemm_frag")
     return out

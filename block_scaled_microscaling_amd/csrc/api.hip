@@ -230,4 +230,53 @@ int mxfp4_gemm_swiglu(const void* A_codes, const void* A_scales, const void* B_c
                                                  static_cast<hipStream_t>(stream)));
 }
 
+int mxfp4_quantize_frag(const void* x_bf16, int64_t M, int64_t K, void* codes_frag,
+                        void* scales_frag, void* stream) {
+  if (!x_bf16 || !codes_frag || !scales_frag) return MXFP4_EINVAL;
+  if (M < 32 || K < 256 || M % 32 != 0 || K % 256 != 0 || M > kMaxDim || K > kMaxGemmK)
+    return MXFP4_EINVAL;
+  if (M * K >= kMaxBytes) return MXFP4_EINVAL;
+  if (!aligned(x_bf16, 16) || !aligned(codes_frag, 16)) return MXFP4_EALIGN;
+  const int dev = check_device();
+  if (dev != MXFP4_OK) return dev;
+  return launch_status(mxfp4::launch_quantize_frag(x_bf16, M, K, codes_frag, scales_frag,
+                                                   static_cast<hipStream_t>(stream)));
+}
+
+int mxfp4_to_frag(const void* codes, const void* scales, int64_t R, int64_t K, void* codes_frag,
+                  void* scales_frag, void* stream) {
+  if (!codes || !scales || !codes_frag || !scales_frag) return MXFP4_EINVAL;
+  if (R < 32 || K < 256 || R % 32 != 0 || K % 256 != 0 || R > kMaxDim || K > kMaxGemmK)
+    return MXFP4_EINVAL;
+  if (R * (K / 2) >= kMaxBytes) return MXFP4_EINVAL;
+  if (!aligned(codes, 16) || !aligned(codes_frag, 16) || !aligned(scales, 4) ||
+      !aligned(scales_frag, 4))
+    return MXFP4_EALIGN;
+  const int dev = check_device();
+  if (dev != MXFP4_OK) return dev;
+  return launch_status(mxfp4::launch_to_frag(codes, scales, R, K, codes_frag, scales_frag,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+int mxfp4_gemm_frag(const void* A_frag, const void* A_scales_frag, const void* B_frag,
+                    const void* B_scales_frag, int64_t M, int64_t N, int64_t K, int out_dtype,
+                    void* C, void* stream) {
+  if (!A_frag || !A_scales_frag || !B_frag || !B_scales_frag || !C) return MXFP4_EINVAL;
+  if (M <= 0 || N <= 0 || K <= 0 || N > kMaxDim || K > kMaxGemmK) return MXFP4_EINVAL;
+  // One workgroup row per 32 rows of A: the grid's y extent is at most 65535.
+  if (K % 256 != 0 || M % 32 != 0 || N % 32 != 0 || M / 32 > 65535) return MXFP4_EINVAL;
+  if (out_dtype != MXFP4_OUT_BF16 && out_dtype != MXFP4_OUT_FP32) return MXFP4_EINVAL;
+  const int64_t out_bytes = out_dtype == MXFP4_OUT_FP32 ? 4 : 2;
+  if (N * (K / 2) >= kMaxBytes || M * N * out_bytes >= kMaxBytes) return MXFP4_EINVAL;
+  if (!aligned(A_frag, 16) || !aligned(B_frag, 16) || !aligned(A_scales_frag, 4) ||
+      !aligned(B_scales_frag, 4) || !aligned(C, 16))
+    return MXFP4_EALIGN;
+  const int dev = check_device();
+  if (dev != MXFP4_OK) return dev;
+  return launch_status(mxfp4::launch_gemm_frag(A_frag, A_scales_frag, B_frag, B_scales_frag,
+                                               (int)M, (int)N, (int)K,
+                                               out_dtype == MXFP4_OUT_FP32, C,
+                                               static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -50,6 +50,16 @@ constexpr int kSkinnyMaxM = 128;
 hipError_t launch_gemm_skinny(const void* A, const void* As, const void* B, const void* Bs,
                               int M, int N, int K, bool out_fp32, void* C, hipStream_t stream);
 
+// Fragment order (the register-ring skinny GEMM's operand order; R % 32 == 0,
+// K % 256 == 0): row-wise quantize writing it, the re-layout of plain
+// MXFP4 bytes into it, and the GEMM reading both operands in it.
+hipError_t launch_quantize_frag(const void* x_bf16, int64_t M, int64_t K, void* codes,
+                                void* scales, hipStream_t stream);
+hipError_t launch_to_frag(const void* codes, const void* scales, int64_t R, int64_t K,
+                          void* codes_f, void* scales_f, hipStream_t stream);
+hipError_t launch_gemm_frag(const void* A, const void* As, const void* B, const void* Bs, int M,
+                            int N, int K, bool out_fp32, void* C, hipStream_t stream);
+
 // One-time per-device set-up of kernel attributes (large LDS allocations).
 hipError_t init_kernels_for_current_device();
 

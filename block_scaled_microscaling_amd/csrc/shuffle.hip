@@ -69,7 +69,52 @@ __global__ __launch_bounds__(kThreads) void shuffle_scales_kernel(const uint8_t*
   out[w] = v;
 }
 
+// Fragment order (the skinny register-ring GEMM's operand order): one thread
+// per 16-byte code chunk o of the output: block o / 256 = t KS + s, slice
+// q = (o / 64) % 4, lane l = o % 64 holding row 32 t + l % 32 and block
+// 4 (l / 32) + q of step s; and one thread per 4-byte scale word w: block
+// w / 64, lane w % 64, scale bytes 8 s + 4 (l / 32) .. + 3 of its row.
+__global__ __launch_bounds__(kThreads) void frag_codes_kernel(const uint8_t* __restrict__ codes,
+                                                              int K, uint4* __restrict__ out,
+                                                              int64_t nchunks16) {
+  const int64_t o = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (o >= nchunks16) return;
+  const int64_t ks_n = K / 256;
+  const int64_t blk = o >> 8;
+  const int64_t t = blk / ks_n, s = blk - t * ks_n;
+  const int q = (int)(o >> 6) & 3, l = (int)o & 63;
+  const int64_t row = 32 * t + (l & 31);
+  out[o] = *reinterpret_cast<const uint4*>(codes + row * (K / 2) + 128 * s + 16 * (4 * (l >> 5) + q));
+}
+
+__global__ __launch_bounds__(kThreads) void frag_scales_kernel(const uint8_t* __restrict__ scales,
+                                                               int K, uint32_t* __restrict__ out,
+                                                               int64_t nwords) {
+  const int64_t w = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (w >= nwords) return;
+  const int64_t ks_n = K / 256;
+  const int64_t blk = w >> 6;
+  const int64_t t = blk / ks_n, s = blk - t * ks_n;
+  const int l = (int)w & 63;
+  const int64_t row = 32 * t + (l & 31);
+  out[w] = *reinterpret_cast<const uint32_t*>(scales + row * (K / 32) + 8 * s + 4 * (l >> 5));
+}
+
 }  // namespace
+
+hipError_t launch_to_frag(const void* codes, const void* scales, int64_t R, int64_t K,
+                          void* codes_f, void* scales_f, hipStream_t stream) {
+  const int64_t n16 = R * K / 32, nw = R * K / 128;
+  hipLaunchKernelGGL(frag_codes_kernel, dim3((unsigned)((n16 + kThreads - 1) / kThreads)),
+                     dim3(kThreads), 0, stream, static_cast<const uint8_t*>(codes), (int)K,
+                     static_cast<uint4*>(codes_f), n16);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(frag_scales_kernel, dim3((unsigned)((nw + kThreads - 1) / kThreads)),
+                     dim3(kThreads), 0, stream, static_cast<const uint8_t*>(scales), (int)K,
+                     static_cast<uint32_t*>(scales_f), nw);
+  return hipGetLastError();
+}
 
 void shuffled_b_sizes(int64_t N, int64_t K, int64_t* code_bytes, int64_t* scale_bytes) {
   const int64_t nt = (N + 255) / 256;

@@ -182,6 +182,43 @@ int mxfp4_gemm_swiglu(const void* A_codes, const void* A_scales, const void* B_c
                       const void* B_scales, int64_t M, int64_t N, int64_t K, void* act_codes,
                       void* act_scales, void* act_bf16, void* stream);
 
+/* Fragment order: an MXFP4 operand re-arranged so that a GEMM keeping its
+ * operands in registers loads each block-scaled MFMA operand as one
+ * contiguous 1 KiB run (the pre-arranged operands of the a4w4 path on
+ * "Integrate MXFP4 hipblaslt GEMM support", #697, Changes list, and
+ * "Initial integration of a4w4 GEMM", #663; the pages give no layout, this
+ * one is the library's own). For X [R, K] (R % 32 == 0, K % 256 == 0), with
+ * tile t = row / 32, r = row % 32, step s = k / 256, KS = K / 256, and block
+ * j = 4 h + q (h < 2, q < 4) of the 8 32-element blocks of the row's step,
+ * lane l = r + 32 h:
+ *   codes  [R * K / 2] bytes: the 16 code bytes of that block at
+ *          (t KS + s) * 4096 + 1024 q + 16 l
+ *   scales [R * K / 32] bytes: its scale at (t KS + s) * 256 + 4 l + q
+ * (same sizes as the plain layout; a permutation of its bytes).
+ *
+ * mxfp4_quantize_frag: mxfp4_quantize with the outputs in fragment order.
+ *   x_bf16 [M, K] row-major BF16 (16-byte aligned); codes_frag 16-byte
+ *   aligned. Requires M >= 32, M % 32 == 0, K % 256 == 0, K <= 2^24,
+ *   M * K < 2^40.
+ * mxfp4_to_frag: plain codes [R, K/2] (16-byte aligned) and scales [R, K/32]
+ *   (4-byte aligned) -> fragment order (same alignments). Requires R >= 32,
+ *   R % 32 == 0, K % 256 == 0, K <= 2^24, R * K / 2 < 2^40.
+ * mxfp4_gemm_frag: mxfp4_gemm with both operands in fragment order (codes
+ *   16-byte, scales 4-byte aligned; C as mxfp4_gemm). Built for few rows of
+ *   A (decode shapes): one 32 x 32 tile of C per workgroup, the K steps
+ *   split between its 8 waves and summed in a fixed order, exactly the
+ *   arithmetic of mxfp4_gemm's M <= 128 kernel, so for M <= 128 the two
+ *   return identical bits. Requires M % 32 == 0, M / 32 <= 65535,
+ *   N % 32 == 0, K % 256 == 0, K <= 2^24.
+ * All three: asynchronous on `stream`; errors as mxfp4_gemm. */
+int mxfp4_quantize_frag(const void* x_bf16, int64_t M, int64_t K, void* codes_frag,
+                        void* scales_frag, void* stream);
+int mxfp4_to_frag(const void* codes, const void* scales, int64_t R, int64_t K, void* codes_frag,
+                  void* scales_frag, void* stream);
+int mxfp4_gemm_frag(const void* A_frag, const void* A_scales_frag, const void* B_frag,
+                    const void* B_scales_frag, int64_t M, int64_t N, int64_t K, int out_dtype,
+                    void* C, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

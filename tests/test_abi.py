@@ -32,9 +32,10 @@ def test_library_exports_every_declared_symbol():
     lib = mx.load_library()
     names = _declared_functions()
     assert names == ["mxfp4_available", "mxfp4_gemm", "mxfp4_gemm_bshuffled",
-                     "mxfp4_gemm_swiglu", "mxfp4_quantize", "mxfp4_quantize_2d",
-                     "mxfp4_quantize_2d_sr", "mxfp4_quantize_async", "mxfp4_quantize_sr",
-                     "mxfp4_shuffle_b", "mxfp4_shuffle_b_sizes", "mxfp4_strerror"]
+                     "mxfp4_gemm_frag", "mxfp4_gemm_swiglu", "mxfp4_quantize",
+                     "mxfp4_quantize_2d", "mxfp4_quantize_2d_sr", "mxfp4_quantize_async",
+                     "mxfp4_quantize_frag", "mxfp4_quantize_sr", "mxfp4_shuffle_b",
+                     "mxfp4_shuffle_b_sizes", "mxfp4_strerror", "mxfp4_to_frag"]
     for n in names:
         assert hasattr(lib, n), n
 
@@ -187,6 +188,10 @@ def test_no_device_reports_unsupported():
     assert mx.mxfp4_gemm_bshuffled(P16, P16, P16, P16, 32, 32, 256, mx.OUT_BF16, P16,
                                    None) == EUNSUPPORTED
     assert mx.mxfp4_quantize_2d_sr(P16, 32, 32, 5, P16, P16, P16, P16, None) == EUNSUPPORTED
+    assert mx.mxfp4_quantize_frag(P16, 32, 256, P16, P16, None) == EUNSUPPORTED
+    assert mx.mxfp4_to_frag(P16, P16, 32, 256, P16, P16, None) == EUNSUPPORTED
+    assert mx.mxfp4_gemm_frag(P16, P16, P16, P16, 32, 32, 256, mx.OUT_BF16, P16,
+                              None) == EUNSUPPORTED
 
 
 def test_tensor_layer_validates_before_calling():
@@ -200,3 +205,37 @@ def test_tensor_layer_validates_before_calling():
         mx.quantize_sr(x, 1)
     with pytest.raises(ValueError):
         mx.quantize_sr(torch.zeros((4, 64), dtype=torch.bfloat16), -1)
+
+
+@pytest.mark.parametrize("M,K", [(0, 256), (16, 256), (48, 256), (32, 128), (32, 288),
+                                 (32, 1 << 25), (1 << 31, 256)])
+def test_frag_quantize_and_relayout_reject_bad_sizes(M, K):
+    assert mx.mxfp4_quantize_frag(P16, M, K, P16, P16, None) == EINVAL
+    assert mx.mxfp4_to_frag(P16, P16, M, K, P16, P16, None) == EINVAL
+
+
+def test_frag_entries_reject_nulls_and_misalignment():
+    assert mx.mxfp4_quantize_frag(None, 32, 256, P16, P16, None) == EINVAL
+    assert mx.mxfp4_quantize_frag(P16, 32, 256, None, P16, None) == EINVAL
+    assert mx.mxfp4_quantize_frag(P16 + 8, 32, 256, P16, P16, None) == EALIGN
+    assert mx.mxfp4_quantize_frag(P16, 32, 256, P16 + 4, P16, None) == EALIGN
+    assert mx.mxfp4_to_frag(P16, None, 32, 256, P16, P16, None) == EINVAL
+    for i, off in ((0, 8), (1, 2), (4, 8), (5, 2)):
+        args = [P16, P16, 32, 256, P16, P16, None]
+        args[i] = P16 + off
+        assert mx.mxfp4_to_frag(*args) == EALIGN
+
+
+@pytest.mark.parametrize("M,N,K", [(0, 32, 256), (32, 0, 256), (16, 32, 256), (32, 48, 256),
+                                   (32, 32, 128), (32, 32, 1 << 25), (32 * 65536, 32, 256)])
+def test_gemm_frag_rejects_bad_sizes(M, N, K):
+    assert mx.mxfp4_gemm_frag(P16, P16, P16, P16, M, N, K, mx.OUT_BF16, P16, None) == EINVAL
+
+
+def test_gemm_frag_rejects_bad_dtype_nulls_and_misalignment():
+    assert mx.mxfp4_gemm_frag(P16, P16, P16, P16, 32, 32, 256, 3, P16, None) == EINVAL
+    assert mx.mxfp4_gemm_frag(P16, P16, None, P16, 32, 32, 256, mx.OUT_BF16, P16, None) == EINVAL
+    for i, off in ((0, 8), (1, 2), (2, 8), (3, 2), (8, 8)):
+        args = [P16, P16, P16, P16, 32, 32, 256, mx.OUT_BF16, P16, None]
+        args[i] = P16 + off
+        assert mx.mxfp4_gemm_frag(*args) == EALIGN

@@ -282,8 +282,8 @@ def test_workload_full_size(name):
 
 @pytest.mark.parametrize("M", [32, 256])
 def test_maximum_k_closed_form(M):
-    """K = 2^24, the largest K the GEMM accepts, on both kernels and on the
-    pre-shuffled path. A is all 1.0 (scale 127); row n of B holds 1.0 at
+    """K = 2^24, the largest K the GEMM accepts, on both kernels, on the
+    pre-shuffled path and (M = 32) on the fragment-order path. A is all 1.0 (scale 127); row n of B holds 1.0 at
     every k with k % 8192 == 2 n (2048 of them) under scale 127 + n % 3, so
     C[m, n] = 2048 * 2^(n % 3) exactly: every K block of the range counts,
     and any offset overflow along K would change the sums."""
@@ -305,3 +305,10 @@ def test_maximum_k_closed_form(M):
     got = mx.gemm_bshuffled(a_codes, a_scales, bc, bs, N, out_dtype=torch.float32)
     torch.cuda.synchronize()
     assert torch.equal(got, want)
+    del bc, bs
+    if M <= 128:
+        af, asf = mx.to_frag(a_codes, a_scales)
+        bf, bsf = mx.to_frag(b_codes, b_scales)
+        got = mx.gemm_frag(af, asf, bf, bsf, M, N, K, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        assert torch.equal(got, want)
