@@ -244,11 +244,18 @@ def main():
     copies = max(1, -(-2 * LLC_BYTES // b_bytes)) if hbm_bound else 1
     weights = [(bc, bs)] + [(bc.clone(), bs.clone()) for _ in range(copies - 1)]
     # Larger GEMMs run on the tile kernel with B pre-shuffled once (part of
-    # the weight preparation, like its quantization); skinny ones (split-K
-    # kernel) take B as is.
+    # the weight preparation, like its quantization). Skinny ones run the
+    # register-ring kernel on fragment-order operands: the weight copies are
+    # re-laid out once, and the activation is quantized straight into
+    # fragment order each step.
     shuffled = not hbm_bound
+    frag = hbm_bound and M % 32 == 0 and K % 256 == 0
     if shuffled:
         bsh = mx.shuffle_b(bc, bs)
+    if frag:
+        weights_f = [mx.to_frag(wb, ws) for wb, ws in weights]
+        af = torch.empty(M * K // 2, dtype=torch.uint8, device=dev)
+        asf = torch.empty(M * K // 32, dtype=torch.uint8, device=dev)
     ac = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
     as_ = torch.empty((M, K // 32), dtype=torch.uint8, device=dev)
     c = torch.empty((M, N), dtype=out_dtype, device=dev)
@@ -257,14 +264,23 @@ def main():
     counter = [0]
 
     def gemm_step(i):
-        wb, ws = weights[i % copies]
-        if shuffled:
+        if frag:
+            wf, wsf = weights_f[i % copies]
+            mx.gemm_frag(af, asf, wf, wsf, M, N, K, out=c)
+        elif shuffled:
             mx.gemm_bshuffled(ac, as_, bsh[0], bsh[1], N, out=c)
         else:
+            wb, ws = weights[i % copies]
             mx.gemm(ac, as_, wb, ws, out=c)
 
+    def quantize_step():
+        if frag:
+            mx.quantize_frag(x, af, asf)
+        else:
+            mx.quantize(x, ac, as_)
+
     def step():
-        mx.quantize(x, ac, as_)
+        quantize_step()
         gemm_step(counter[0])
         counter[0] += 1
 
@@ -310,7 +326,9 @@ def main():
             once(i)
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
-        hold(5.0)
+        # Long enough for the host to queue every launch first, also under a
+        # profiler, which slows each launch to tens of microseconds.
+        hold(5.0 + 0.06 * reps)
         e0.record(stream)
         for i in range(reps):
             once(i)
@@ -320,17 +338,22 @@ def main():
 
     # The step's GEMM (skinny: B rotated through its copies, so each launch
     # reads B from HBM) and the step's quantize.
-    g_ms = time_alone(gemm_step, "gemm", reps=10 * copies if hbm_bound else 20)
-    q_ms = time_alone(lambda i: mx.quantize(x, ac, as_), "quantize")
+    reps_gemm = 10 * copies if hbm_bound else 20
+    g_ms = time_alone(gemm_step, "gemm", reps=reps_gemm)
+    q_ms = time_alone(lambda i: quantize_step(), "quantize")
     gemm_tflops = flops / (g_ms * 1e-3) / 1e12
     quant_gbps = q_bytes / (q_ms * 1e-3) / 1e9
 
-    # The GEMM on B in its plain layout, timed alone (the step's GEMM when
-    # the workload is skinny).
-    gplain_ms = time_alone(lambda i: mx.mxfp4_gemm(ac.data_ptr(), as_.data_ptr(), bc.data_ptr(),
-                                                 bs.data_ptr(), M, N, K, w.out_dtype,
-                                                 c.data_ptr(), stream.cuda_stream),
-                           "mxfp4_gemm")
+    # The GEMM on operands in their plain row-major layout, timed alone (for
+    # skinny workloads over the same rotated weight copies), and the
+    # row-major quantize beside the fragment-order one.
+    def plain_gemm(i):
+        wb, ws = weights[i % copies]
+        return mx.mxfp4_gemm(ac.data_ptr(), as_.data_ptr(), wb.data_ptr(), ws.data_ptr(), M, N, K,
+                             w.out_dtype, c.data_ptr(), stream.cuda_stream)
+    mx.quantize(x, ac, as_)
+    gplain_ms = time_alone(plain_gemm, "mxfp4_gemm", reps=reps_gemm)
+    qplain_ms = time_alone(lambda i: mx.quantize(x, ac, as_), "quantize") if frag else q_ms
 
     seed = 0x5EED
     qsr_ms = time_alone(lambda i: mx.mxfp4_quantize_sr(x.data_ptr(), M, K, seed, ac.data_ptr(),
@@ -380,9 +403,11 @@ def main():
         "dtype": "mxfp4",
         "data": "synthetic",
         "config": {
-            "workload": (f"{w.name}: quantize A[{M},{K}] BF16 -> MXFP4, then GEMM "
+            "workload": (f"{w.name}: quantize A[{M},{K}] BF16 -> MXFP4"
+                         f"{' (fragment order)' if frag else ''}, then GEMM "
                          f"{M}x{N}x{K} against pre-quantized"
-                         f"{', pre-shuffled' if shuffled else ''} B[{N},{K}], "
+                         f"{', pre-shuffled' if shuffled else ''}"
+                         f"{', fragment-order' if frag else ''} B[{N},{K}], "
                          f"{'fp32' if w.out_dtype else 'bf16'} out"),
             "M": M, "N": N, "K": K,
             "out_dtype": "fp32" if w.out_dtype else "bf16",
@@ -392,9 +417,12 @@ def main():
         "quantize_gbps": quant_gbps,
         "quantize_ms": q_ms,
         "quantize_hbm_frac": quant_gbps / HBM_PEAK_GBPS,
-        "gemm_b_layout": "pre-shuffled" if shuffled else "plain",
+        "gemm_b_layout": ("pre-shuffled" if shuffled else
+                          "fragment order (A and B)" if frag else "plain"),
         "gemm_plain_b_ms": gplain_ms,
         "gemm_plain_b_tflops": flops / (gplain_ms * 1e-3) / 1e12,
+        "gemm_plain_b_gbps_algorithmic": gemm_bytes / (gplain_ms * 1e-3) / 1e9,
+        "quantize_row_major_ms": qplain_ms,
         "quantize_sr_ms": qsr_ms,
         "quantize_sr_gbps": gbps(q_bytes, qsr_ms),
         "quantize_2d_ms": q2_ms,
