@@ -11,22 +11,23 @@
 // arithmetic is the one of quantize.hip (integer amax of |bits|, scale byte
 // = max(E_field(amax) - 2, 0), v_cvt_scalef32_pk_fp4_bf16 for RNE E2M1).
 //
-// Work mapping: a workgroup of 256 threads handles one 256-row x 128-column
-// tile at a time. For round to nearest the grid is persistent (two
-// workgroups per CU) and each workgroup loads its next tile into registers
-// while it finishes the last; the stochastic variant launches one workgroup
-// per tile.
-//   Row phase: load i of thread t reads the 16-byte chunk t % 16 of row
-//   16 i + t / 16: 16 lanes per 256-byte row segment, so each wave load
-//   fetches 4 rows x 2 whole lines; four consecutive lanes hold one MX block
-//   (amax finished with two quad DPP moves). The tile is parked in LDS with
-//   rows padded to 272 bytes.
-//   Column phase: thread t takes columns 2 (t % 64), +1 and row blocks
-//   2 (t / 64), +1: 32 dword reads per row block (both columns at once), an
-//   integer amax per column, byte permutes pairing consecutive rows, 16
-//   conversions per column block. The column codes and scales are parked in
-//   LDS again and written with 8 lanes per 128-byte column segment: whole
-//   cache lines per store.
+// Work mapping: a workgroup of 2 C threads handles one 256-row x C-column
+// tile at a time (C = 256 for round to nearest, 128 for stochastic
+// rounding). For round to nearest the grid is persistent (one workgroup per
+// CU) and each workgroup loads its next tile into registers while it
+// finishes the last; the stochastic variant launches one workgroup per tile.
+//   Row phase: load i of thread t reads the 16-byte chunk t % (C / 8) of row
+//   16 i + t / (C / 8): C / 8 lanes per 2C-byte row segment, so each wave
+//   load fetches whole lines; four consecutive lanes hold one MX block
+//   (amax finished with two quad DPP moves), and a row's codes of the tile
+//   are C / 2 bytes (one whole line at C = 256). The tile is parked in LDS
+//   with rows padded by 16 bytes.
+//   Column phase: thread t takes columns 2 (t % (C / 2)), +1 and row blocks
+//   2 (t / (C / 2)), +1: 32 dword reads per row block (both columns at
+//   once), an integer amax per column, byte permutes pairing consecutive
+//   rows, 16 conversions per column block. The column codes and scales are
+//   parked in LDS again and written with 8 lanes per 128-byte column
+//   segment: whole cache lines per store.
 // Edge tiles (M or K not multiples of the tile) mask whole 32-element blocks.
 //
 // The stochastic-rounding variant (kSR) keeps the mapping and replaces only
@@ -49,10 +50,14 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;
 constexpr int kRows = 256;
-constexpr int kCols = 128;
-constexpr int kLdsRow = 2 * kCols + 16;  // 272 bytes
+// Tile width kC (128 or 256 columns) and its workgroup of 2 kC threads.
+template <int kC>
+struct Geom {
+  static constexpr int kThreads = 2 * kC;
+  static constexpr int kSeg = kC / 8;         // lanes per row segment (16 bytes each)
+  static constexpr int kLdsRow = 2 * kC + 16;  // padded LDS row, bytes
+};
 
 __device__ __forceinline__ u16x2_t abs_pair(uint32_t w) {
   return __builtin_bit_cast(u16x2_t, w & 0x7FFF7FFFu);
@@ -86,15 +91,17 @@ __device__ __forceinline__ uint32_t swap_pair(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);
 }
 
-// Loads of one tile into registers: load i covers rows 16 i + t / 16,
-// 16-byte chunk t % 16 (zeros outside the matrix).
+// Loads of one tile into registers: load i covers rows 16 i + t / kSeg,
+// 16-byte chunk t % kSeg (zeros outside the matrix).
+template <int kC>
 __device__ __forceinline__ void load_tile(const uint8_t* __restrict__ x, int M, int K, int m0,
                                           int c0, int t, u32x4_t (&v)[16]) {
+  constexpr int kSeg = Geom<kC>::kSeg;
   const int64_t row_bytes = 2 * (int64_t)K;
-  const int col = c0 + 8 * (t & 15);
+  const int col = c0 + 8 * (t % kSeg);
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    const int m = m0 + 16 * i + (t >> 4);
+    const int m = m0 + 16 * i + t / kSeg;
     v[i] = (m < M && col < K)
                ? __builtin_nontemporal_load(
                      reinterpret_cast<const u32x4_t*>(x + m * row_bytes + 2 * (int64_t)col))
@@ -106,11 +113,15 @@ __device__ __forceinline__ void load_tile(const uint8_t* __restrict__ x, int M, 
 // the tile grid) and issues the next tile's loads as soon as the current
 // tile's rows are in LDS, so they are in flight during its column phase and
 // stores.
-template <bool kSR>
-__global__ __launch_bounds__(kThreads) void quantize_2d_kernel(
+template <bool kSR, int kC>
+__global__ __launch_bounds__(Geom<kC>::kThreads) void quantize_2d_kernel(
     const uint8_t* __restrict__ x, int M, int K, uint8_t* __restrict__ codes_row,
     uint8_t* __restrict__ scales_row, uint8_t* __restrict__ codes_col,
     uint8_t* __restrict__ scales_col, uint32_t key0, uint32_t key1) {
+  constexpr int kCols = kC;
+  constexpr int kThreads = Geom<kC>::kThreads;
+  constexpr int kSeg = Geom<kC>::kSeg;
+  constexpr int kLdsRow = Geom<kC>::kLdsRow;
   __shared__ __align__(16) uint8_t tile[kRows * kLdsRow];
   const int t = threadIdx.x;
   const int tiles_x = (K + kCols - 1) / kCols;
@@ -118,19 +129,19 @@ __global__ __launch_bounds__(kThreads) void quantize_2d_kernel(
   int p = blockIdx.x;
   if (p >= total) return;
   u32x4_t v[16];
-  load_tile(x, M, K, (p / tiles_x) * kRows, (p % tiles_x) * kCols, t, v);
+  load_tile<kC>(x, M, K, (p / tiles_x) * kRows, (p % tiles_x) * kCols, t, v);
   for (; p < total; p += gridDim.x) {
     const int m0 = (p / tiles_x) * kRows;
     const int c0 = (p % tiles_x) * kCols;
     // Row phase: park the rows in LDS, encode them row-wise.
     {
-      const int chunk = t & 15;
+      const int chunk = t % kSeg;
       const int col = c0 + 8 * chunk;
       const int odd = t & 1;
       uint32_t rnd_next[2] = {0u, 0u};  // kSR: the odd load's bytes of a pair
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int r = 16 * i + (t >> 4);
+        const int r = 16 * i + t / kSeg;
         *reinterpret_cast<u32x4_t*>(tile + r * kLdsRow + 16 * chunk) = v[i];
         const u32x4_t q = v[i];
         const u16x2_t mx = max2(max2(abs_pair(q[0]), abs_pair(q[1])),
@@ -142,7 +153,7 @@ __global__ __launch_bounds__(kThreads) void quantize_2d_kernel(
           // Draws for the pair of loads (i, i + 1), taken at the even one.
           uint32_t rnd[2];
           if ((i & 1) == 0) {
-            const uint32_t drow = (uint32_t)(m0 + 16 * (i + odd) + (t >> 4));
+            const uint32_t drow = (uint32_t)(m0 + 16 * (i + odd) + t / kSeg);
             const Draw d = philox4x32_10((uint32_t)(col / 32), drow, kDirRowwise,
                                          (uint32_t)((t >> 1) & 1), key0, key1);
             const uint32_t got0 = swap_pair(odd ? d.w[0] : d.w[2]);
@@ -169,15 +180,15 @@ __global__ __launch_bounds__(kThreads) void quantize_2d_kernel(
     // The registers are free again: start the next tile's loads.
     if (p + (int)gridDim.x < total) {
       const int pn = p + gridDim.x;
-      load_tile(x, M, K, (pn / tiles_x) * kRows, (pn % tiles_x) * kCols, t, v);
+      load_tile<kC>(x, M, K, (pn / tiles_x) * kRows, (pn % tiles_x) * kCols, t, v);
     }
     __syncthreads();
 
     // Column phase: columns c0 + 2 cp, +1; row blocks 2 bp, 2 bp + 1. The
     // codes and scales are parked in LDS (the tile is dead by then) and
     // written out with whole lines: 8 lanes per 128-byte column segment.
-    const int cp = t & 63;
-    const int bp = t >> 6;
+    const int cp = t % (kCols / 2);
+    const int bp = t / (kCols / 2);
     u32x4_t out[2][2];
     uint32_t sbyte[2][2];
 #pragma unroll
@@ -245,7 +256,7 @@ __global__ __launch_bounds__(kThreads) void quantize_2d_kernel(
     const int rows_valid = min(kRows, M - m0);  // multiple of 32
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int c = 32 * j + (t >> 3);
+      const int c = (kThreads / 8) * j + (t >> 3);
       const int part = t & 7;  // 16-byte part = row block
       const int k = c0 + c;
       if (k < K && 32 * part < rows_valid)
@@ -278,11 +289,17 @@ __global__ __launch_bounds__(kThreads) void quantize_2d_kernel(
 }  // namespace
 
 // Round to nearest: a persistent grid of two workgroups per CU (69.6 KiB of
-// LDS each). Stochastic rounding is bound by its VALU work, where the
+// LDS each). Measured on 8192 x 8192: 43.9 us; 256 x 256 tiles (whole lines
+// of row-wise codes too, 512 threads, 132 KiB of LDS, one workgroup per CU)
+// took 46.0 us. Stochastic rounding is bound by its VALU work, where the
 // prefetch only adds register pressure (measured 4% slower): one tile per
 // workgroup, the loop runs once.
-static hipError_t grid_2d(int M, int K, bool persistent, dim3& grid) {
-  const int64_t total = (int64_t)((K + kCols - 1) / kCols) * ((M + kRows - 1) / kRows);
+constexpr int kColsRn = 128;
+constexpr int kColsSr = 128;
+constexpr int kWorkgroupsPerCu = 2;
+
+static hipError_t grid_2d(int M, int K, int cols, bool persistent, dim3& grid) {
+  const int64_t total = (int64_t)((K + cols - 1) / cols) * ((M + kRows - 1) / kRows);
   if (!persistent) {
     grid = dim3((unsigned)total);
     return hipSuccess;
@@ -290,17 +307,18 @@ static hipError_t grid_2d(int M, int K, bool persistent, dim3& grid) {
   int workers = 0;
   const hipError_t e = device_workers(workers);
   if (e != hipSuccess) return e;
-  grid = dim3((unsigned)(total < 2 * workers ? total : 2 * workers));
+  const int64_t cap = (int64_t)kWorkgroupsPerCu * workers;
+  grid = dim3((unsigned)(total < cap ? total : cap));
   return hipSuccess;
 }
 
 hipError_t launch_quantize_2d(const void* x_bf16, int M, int K, void* codes_row, void* scales_row,
                               void* codes_col, void* scales_col, hipStream_t stream) {
   dim3 grid;
-  const hipError_t e = grid_2d(M, K, true, grid);
+  const hipError_t e = grid_2d(M, K, kColsRn, true, grid);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(quantize_2d_kernel<false>, grid, dim3(kThreads), 0, stream,
-                     static_cast<const uint8_t*>(x_bf16), M, K,
+  hipLaunchKernelGGL((quantize_2d_kernel<false, kColsRn>), grid, dim3(Geom<kColsRn>::kThreads), 0,
+                     stream, static_cast<const uint8_t*>(x_bf16), M, K,
                      static_cast<uint8_t*>(codes_row), static_cast<uint8_t*>(scales_row),
                      static_cast<uint8_t*>(codes_col), static_cast<uint8_t*>(scales_col), 0u, 0u);
   return hipGetLastError();
@@ -310,10 +328,10 @@ hipError_t launch_quantize_2d_sr(const void* x_bf16, int M, int K, uint64_t seed
                                  void* scales_row, void* codes_col, void* scales_col,
                                  hipStream_t stream) {
   dim3 grid;
-  const hipError_t e = grid_2d(M, K, false, grid);
+  const hipError_t e = grid_2d(M, K, kColsSr, false, grid);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(quantize_2d_kernel<true>, grid, dim3(kThreads), 0, stream,
-                     static_cast<const uint8_t*>(x_bf16), M, K,
+  hipLaunchKernelGGL((quantize_2d_kernel<true, kColsSr>), grid, dim3(Geom<kColsSr>::kThreads), 0,
+                     stream, static_cast<const uint8_t*>(x_bf16), M, K,
                      static_cast<uint8_t*>(codes_row), static_cast<uint8_t*>(scales_row),
                      static_cast<uint8_t*>(codes_col), static_cast<uint8_t*>(scales_col),
                      (uint32_t)seed, (uint32_t)(seed >> 32));

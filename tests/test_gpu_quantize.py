@@ -172,9 +172,12 @@ def _assert_same_2d(bits):
 
 
 @pytest.mark.parametrize("M,K", [(32, 32), (128, 128), (256, 384), (160, 96), (4128, 7936),
-                                 (96, 4128), (1056, 352)])
+                                 (96, 4128), (1056, 352), (288, 800), (512, 1024)])
 def test_quantize_2d_random(M, K):
-    """Random finite bit patterns; shapes with whole and ragged 128 x 128 tiles."""
+    """Random finite bit patterns; shapes with whole and ragged 256 x 256
+    tiles (the kernel's), down to a single 32-element block past the last
+    whole tile (K = 800), and more tiles than one pass of the persistent grid
+    (4128 x 7936)."""
     announce(f"quantize_2d random {M}x{K}")
     _assert_same_2d(random_bf16_bits((M, K), seed=M * 7 + K))
 
