@@ -267,7 +267,8 @@ int mxfp4_gemm_frag(const void* A_frag, const void* A_scales_frag, const void* B
   if (K % 256 != 0 || M % 32 != 0 || N % 32 != 0 || M / 32 > 65535) return MXFP4_EINVAL;
   if (out_dtype != MXFP4_OUT_BF16 && out_dtype != MXFP4_OUT_FP32) return MXFP4_EINVAL;
   const int64_t out_bytes = out_dtype == MXFP4_OUT_FP32 ? 4 : 2;
-  if (N * (K / 2) >= kMaxBytes || M * N * out_bytes >= kMaxBytes) return MXFP4_EINVAL;
+  if (M * (K / 2) >= kMaxBytes || N * (K / 2) >= kMaxBytes || M * N * out_bytes >= kMaxBytes)
+    return MXFP4_EINVAL;
   if (!aligned(A_frag, 16) || !aligned(B_frag, 16) || !aligned(A_scales_frag, 4) ||
       !aligned(B_scales_frag, 4) || !aligned(C, 16))
     return MXFP4_EALIGN;

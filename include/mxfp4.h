@@ -209,7 +209,7 @@ int mxfp4_gemm_swiglu(const void* A_codes, const void* A_scales, const void* B_c
  *   split between its 8 waves and summed in a fixed order, exactly the
  *   arithmetic of mxfp4_gemm's M <= 128 kernel, so for M <= 128 the two
  *   return identical bits. Requires M % 32 == 0, M / 32 <= 65535,
- *   N % 32 == 0, K % 256 == 0, K <= 2^24.
+ *   N % 32 == 0, K % 256 == 0, K <= 2^24, each buffer < 2^40 bytes.
  * All three: asynchronous on `stream`; errors as mxfp4_gemm. */
 int mxfp4_quantize_frag(const void* x_bf16, int64_t M, int64_t K, void* codes_frag,
                         void* scales_frag, void* stream);
