@@ -47,5 +47,35 @@ def build(verbose=True):
     return LIB
 
 
+# Host-only AddressSanitizer: the device code is built as usual and the host
+# code (the C ABI's argument checks, launchers, per-device state) is
+# instrumented. Loading the result needs the matching runtime preloaded
+# (asan_runtime()). Each sanitizer flag applies to the host pass only.
+ASAN_HOST_FLAGS = "-Xarch_host -fsanitize=address -Xarch_host -fno-omit-frame-pointer"
+
+
+def asan_runtime():
+    """Path of clang's shared ASan runtime next to hipcc, or None."""
+    hipcc = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")
+    res = subprocess.run([hipcc, "-print-file-name=libclang_rt.asan-x86_64.so"],
+                         capture_output=True, text=True)
+    path = res.stdout.strip()
+    return path if res.returncode == 0 and os.path.isabs(path) and os.path.exists(path) else None
+
+
+def build_asan(out, verbose=False):
+    """Compile the library with host-side ASan into `out`."""
+    cmd = hipcc_command(str(out))
+    cmd = cmd[:1] + ["-O1", "-g"] + [a for a in cmd[1:] if a != "-O3"]
+    cmd += ASAN_HOST_FLAGS.split() + ["-shared-libasan"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr + "\n")
+        raise subprocess.CalledProcessError(res.returncode, cmd)
+    return str(out)
+
+
 if __name__ == "__main__":
     build()
