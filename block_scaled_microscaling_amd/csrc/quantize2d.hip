@@ -109,15 +109,31 @@ __device__ __forceinline__ void load_tile(const uint8_t* __restrict__ x, int M, 
   }
 }
 
-// Persistent: workgroup g takes tiles g, g + gridDim.x, ... (row-major over
-// the tile grid) and issues the next tile's loads as soon as the current
+// Visit q of the tile sequence -> tile id (row-major over the tile grid),
+// or -1 past the last tile. Workgroups take visits g, g + gridDim.x, ...
+// and workgroup g runs on XCD g % 8. The row-wise codes of a tile cover half
+// of each 128-byte line (C = 128); the other half belongs to the tile to its
+// right. With pair_xcd (a grid that is a multiple of 16) those two tiles are
+// visits q and q + 8 of one round, i.e. workgroups g and g + 8 on the same
+// XCD at the same time, so the two halves of a line meet in one L2 instead
+// of leaving two L2s as partial lines. Visits are numbered past `total` up
+// to a multiple of 16; the map is a bijection on those.
+__device__ __forceinline__ int tile_of_visit(int q, int total, bool pair_xcd) {
+  if (!pair_xcd) return q < total ? q : -1;
+  const int r = q >> 3, xcd = q & 7;
+  const int tile = 2 * (((r >> 1) << 3) + xcd) + (r & 1);
+  return tile < total ? tile : -1;
+}
+
+// Persistent: workgroup g takes visits g, g + gridDim.x, ... (tiles by
+// tile_of_visit) and issues the next tile's loads as soon as the current
 // tile's rows are in LDS, so they are in flight during its column phase and
 // stores.
 template <bool kSR, int kC>
 __global__ __launch_bounds__(Geom<kC>::kThreads) void quantize_2d_kernel(
     const uint8_t* __restrict__ x, int M, int K, uint8_t* __restrict__ codes_row,
     uint8_t* __restrict__ scales_row, uint8_t* __restrict__ codes_col,
-    uint8_t* __restrict__ scales_col, uint32_t key0, uint32_t key1) {
+    uint8_t* __restrict__ scales_col, uint32_t key0, uint32_t key1, bool pair_xcd) {
   constexpr int kCols = kC;
   constexpr int kThreads = Geom<kC>::kThreads;
   constexpr int kSeg = Geom<kC>::kSeg;
@@ -126,11 +142,19 @@ __global__ __launch_bounds__(Geom<kC>::kThreads) void quantize_2d_kernel(
   const int t = threadIdx.x;
   const int tiles_x = (K + kCols - 1) / kCols;
   const int total = tiles_x * ((M + kRows - 1) / kRows);
-  int p = blockIdx.x;
-  if (p >= total) return;
+  // Visit order q -> tile p (pair_xcd: see tile_of_visit); the loop and
+  // its prefetch skip visit numbers that map past the last tile.
+  const int qend = pair_xcd ? (total + 15) & ~15 : total;
+  int q = blockIdx.x;
+  int p = tile_of_visit(q, total, pair_xcd);
+  while (q < qend && p < 0) {
+    q += gridDim.x;
+    p = tile_of_visit(q, total, pair_xcd);
+  }
+  if (q >= qend) return;
   u32x4_t v[16];
   load_tile<kC>(x, M, K, (p / tiles_x) * kRows, (p % tiles_x) * kCols, t, v);
-  for (; p < total; p += gridDim.x) {
+  for (;;) {
     const int m0 = (p / tiles_x) * kRows;
     const int c0 = (p % tiles_x) * kCols;
     // Row phase: park the rows in LDS, encode them row-wise.
@@ -178,10 +202,13 @@ __global__ __launch_bounds__(Geom<kC>::kThreads) void quantize_2d_kernel(
       }
     }
     // The registers are free again: start the next tile's loads.
-    if (p + (int)gridDim.x < total) {
-      const int pn = p + gridDim.x;
-      load_tile<kC>(x, M, K, (pn / tiles_x) * kRows, (pn % tiles_x) * kCols, t, v);
+    int qn = q + (int)gridDim.x;
+    int pn = tile_of_visit(qn, total, pair_xcd);
+    while (qn < qend && pn < 0) {
+      qn += gridDim.x;
+      pn = tile_of_visit(qn, total, pair_xcd);
     }
+    if (qn < qend) load_tile<kC>(x, M, K, (pn / tiles_x) * kRows, (pn % tiles_x) * kCols, t, v);
     __syncthreads();
 
     // Column phase: columns c0 + 2 cp, +1; row blocks 2 bp, 2 bp + 1. The
@@ -283,15 +310,19 @@ __global__ __launch_bounds__(Geom<kC>::kThreads) void quantize_2d_kernel(
     // Every thread's column stores have read the staging area before the
     // next tile's rows overwrite it.
     __syncthreads();
+    if (qn >= qend) break;
+    q = qn;
+    p = pn;
   }
 }
 
 }  // namespace
 
 // Round to nearest: a persistent grid of two workgroups per CU (69.6 KiB of
-// LDS each). Measured on 8192 x 8192: 43.9 us; 256 x 256 tiles (whole lines
-// of row-wise codes too, 512 threads, 132 KiB of LDS, one workgroup per CU)
-// took 46.0 us. Stochastic rounding is bound by its VALU work, where the
+// LDS each), tiles visited in line-sharing pairs (tile_of_visit). Measured
+// on 8192 x 8192: 41.7 us (43.6 us visiting tiles in plain order); 256 x
+// 256 tiles (whole lines of row-wise codes too, 512 threads, 132 KiB of
+// LDS, one workgroup per CU) took 46.0 us. Stochastic rounding is bound by its VALU work, where the
 // prefetch only adds register pressure (measured 4% slower): one tile per
 // workgroup, the loop runs once.
 constexpr int kColsRn = 128;
@@ -320,7 +351,8 @@ hipError_t launch_quantize_2d(const void* x_bf16, int M, int K, void* codes_row,
   hipLaunchKernelGGL((quantize_2d_kernel<false, kColsRn>), grid, dim3(Geom<kColsRn>::kThreads), 0,
                      stream, static_cast<const uint8_t*>(x_bf16), M, K,
                      static_cast<uint8_t*>(codes_row), static_cast<uint8_t*>(scales_row),
-                     static_cast<uint8_t*>(codes_col), static_cast<uint8_t*>(scales_col), 0u, 0u);
+                     static_cast<uint8_t*>(codes_col), static_cast<uint8_t*>(scales_col), 0u, 0u,
+                     grid.x % 16 == 0);
   return hipGetLastError();
 }
 
@@ -334,7 +366,7 @@ hipError_t launch_quantize_2d_sr(const void* x_bf16, int M, int K, uint64_t seed
                      stream, static_cast<const uint8_t*>(x_bf16), M, K,
                      static_cast<uint8_t*>(codes_row), static_cast<uint8_t*>(scales_row),
                      static_cast<uint8_t*>(codes_col), static_cast<uint8_t*>(scales_col),
-                     (uint32_t)seed, (uint32_t)(seed >> 32));
+                     (uint32_t)seed, (uint32_t)(seed >> 32), false);
   return hipGetLastError();
 }
 
