@@ -262,9 +262,12 @@ int mxfp4_gemm_frag(const void* A_frag, const void* A_scales_frag, const void* B
                     const void* B_scales_frag, int64_t M, int64_t N, int64_t K, int out_dtype,
                     void* C, void* stream) {
   if (!A_frag || !A_scales_frag || !B_frag || !B_scales_frag || !C) return MXFP4_EINVAL;
-  if (M <= 0 || N <= 0 || K <= 0 || N > kMaxDim || K > kMaxGemmK) return MXFP4_EINVAL;
-  // One workgroup row per 32 rows of A: the grid's y extent is at most 65535.
-  if (K % 256 != 0 || M % 32 != 0 || N % 32 != 0 || M / 32 > 65535) return MXFP4_EINVAL;
+  if (M <= 0 || N <= 0 || K <= 0 || M > kMaxDim || N > kMaxDim || K > kMaxGemmK)
+    return MXFP4_EINVAL;
+  if (K % 256 != 0 || M % 32 != 0 || N % 32 != 0) return MXFP4_EINVAL;
+  // Workgroup rows hold up to three 32-row tiles of A; the grid's y extent
+  // (groups of tiles) is at most 65535.
+  if ((M / 32 + 2) / 3 > 65535) return MXFP4_EINVAL;
   if (out_dtype != MXFP4_OUT_BF16 && out_dtype != MXFP4_OUT_FP32) return MXFP4_EINVAL;
   const int64_t out_bytes = out_dtype == MXFP4_OUT_FP32 ? 4 : 2;
   if (M * (K / 2) >= kMaxBytes || N * (K / 2) >= kMaxBytes || M * N * out_bytes >= kMaxBytes)

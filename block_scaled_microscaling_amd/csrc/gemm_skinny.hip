@@ -64,6 +64,7 @@ constexpr int kSlotBytes = 2 * kCodeBytes + 2 * kScaleBytes;
 constexpr int kWaveBytes = 2 * kSlotBytes;
 constexpr int kLdsBytes = kWaves * kWaveBytes;        // 136 KiB
 constexpr int kLoadsPerStep = 10;                     // 4 + 4 code, 2 scale instructions
+constexpr int kMaxFragTiles = 3;                      // tiles of A per fragment-order workgroup
 
 static_assert(kWaves * kTile * kTile * 4 <= kLdsBytes, "reduction buffer fits the ring");
 
@@ -217,12 +218,17 @@ __global__ __launch_bounds__(kThreads) void gemm_skinny_kernel(
 // compiler-visible loads, so the compiler's in-order vmcnt waits are exact;
 // loads are unconditional (past the wave's last step they re-read that
 // step) so that no branch makes those waits conservative.
-constexpr int kDepth = 4;
-
-template <bool kOutFp32>
+// Up to three 32-row tiles of A per workgroup (kMT): the B fragments of a
+// step are loaded once and used for every tile of A, and each tile's
+// accumulator sees exactly the sequence of MFMAs of a one-tile kernel (same
+// bits). Steps in flight per wave: kDepth (4 for one tile; 2 beyond, which
+// keeps A's extra fragments within two waves' share of the register file:
+// 160 and 218 VGPRs for two and three tiles, no spills; four tiles spilled
+// 30 VGPRs).
+template <bool kOutFp32, int kMT, int kDepth>
 __global__ __launch_bounds__(kThreads) void gemm_frag_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ As,
-    const uint8_t* __restrict__ B, const uint8_t* __restrict__ Bs, int N, int K,
+    const uint8_t* __restrict__ B, const uint8_t* __restrict__ Bs, int m_tile0, int N, int K,
     void* __restrict__ C) {
   __shared__ __align__(16) float red[kWaves * 1024];
   typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
@@ -231,14 +237,17 @@ __global__ __launch_bounds__(kThreads) void gemm_frag_kernel(
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const int steps = K / kStepK;
   const int nst = (steps - wave + kWaves - 1) / kWaves;
+  const int mt0 = m_tile0 + (int)blockIdx.y * kMT;  // first tile of A
   // Blocks of this workgroup's tiles; lane offsets inside a block.
-  const u32x4_t* pa = reinterpret_cast<const u32x4_t*>(A) + (int64_t)blockIdx.y * steps * 256 + lane;
+  const u32x4_t* pa = reinterpret_cast<const u32x4_t*>(A) + (int64_t)mt0 * steps * 256 + lane;
   const u32x4_t* pb = reinterpret_cast<const u32x4_t*>(B) + (int64_t)blockIdx.x * steps * 256 + lane;
-  const uint32_t* psa = reinterpret_cast<const uint32_t*>(As) + (int64_t)blockIdx.y * steps * 64 + lane;
+  const uint32_t* psa = reinterpret_cast<const uint32_t*>(As) + (int64_t)mt0 * steps * 64 + lane;
   const uint32_t* psb = reinterpret_cast<const uint32_t*>(Bs) + (int64_t)blockIdx.x * steps * 64 + lane;
+  const int64_t a_tile = (int64_t)steps * 256;  // u32x4 per tile of A codes
+  const int64_t s_tile = (int64_t)steps * 64;   // words per tile of A scales
 
-  u32x4_t fa[kDepth][4], fb[kDepth][4];
-  uint32_t sa[kDepth], sb[kDepth];
+  u32x4_t fa[kDepth][kMT][4], fb[kDepth][4];
+  uint32_t sa[kDepth][kMT], sb[kDepth];
   int last = wave + kWaves * (nst > 0 ? nst - 1 : 0);
   last = last < steps ? last : steps - 1;
   auto step_of = [&](int j) {
@@ -252,21 +261,30 @@ __global__ __launch_bounds__(kThreads) void gemm_frag_kernel(
     for (int q = 0; q < 4; ++q) fb[d][q] = __builtin_nontemporal_load(pb + (st * 4 + q) * 64);
     sb[d] = __builtin_nontemporal_load(psb + st * 64);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) fa[d][q] = pa[(st * 4 + q) * 64];
-    sa[d] = psa[st * 64];
-  };
-  v16f_t acc = v16f_t{};
-  auto compute = [&](int d) {
-    uint4 xa[4], xb[4];
+    for (int m = 0; m < kMT; ++m) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      xa[q] = make_uint4(fa[d][q].x, fa[d][q].y, fa[d][q].z, fa[d][q].w);
-      xb[q] = make_uint4(fb[d][q].x, fb[d][q].y, fb[d][q].z, fb[d][q].w);
+      for (int q = 0; q < 4; ++q) fa[d][m][q] = pa[m * a_tile + (st * 4 + q) * 64];
+      sa[d][m] = psa[m * s_tile + st * 64];
     }
-    acc = mfma_fp4<0, 0>(xb[0], xa[0], acc, sb[d], sa[d]);
-    acc = mfma_fp4<1, 1>(xb[1], xa[1], acc, sb[d], sa[d]);
-    acc = mfma_fp4<2, 2>(xb[2], xa[2], acc, sb[d], sa[d]);
-    acc = mfma_fp4<3, 3>(xb[3], xa[3], acc, sb[d], sa[d]);
+  };
+  v16f_t acc[kMT];
+#pragma unroll
+  for (int m = 0; m < kMT; ++m) acc[m] = v16f_t{};
+  auto compute = [&](int d) {
+    uint4 xb[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) xb[q] = make_uint4(fb[d][q].x, fb[d][q].y, fb[d][q].z, fb[d][q].w);
+#pragma unroll
+    for (int m = 0; m < kMT; ++m) {
+      uint4 xa[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        xa[q] = make_uint4(fa[d][m][q].x, fa[d][m][q].y, fa[d][m][q].z, fa[d][m][q].w);
+      acc[m] = mfma_fp4<0, 0>(xb[0], xa[0], acc[m], sb[d], sa[d][m]);
+      acc[m] = mfma_fp4<1, 1>(xb[1], xa[1], acc[m], sb[d], sa[d][m]);
+      acc[m] = mfma_fp4<2, 2>(xb[2], xa[2], acc[m], sb[d], sa[d][m]);
+      acc[m] = mfma_fp4<3, 3>(xb[3], xa[3], acc[m], sb[d], sa[d][m]);
+    }
   };
 
 #pragma unroll
@@ -283,8 +301,39 @@ __global__ __launch_bounds__(kThreads) void gemm_frag_kernel(
   for (int d = 0; d < kDepth; ++d)
     if (i + d < nst) compute(d);
 
-  reduce_store<kOutFp32>(red, acc, wave, lane, (int)blockIdx.y * kTile, (int)blockIdx.x * kTile,
-                         N, C);
+#pragma unroll
+  for (int m = 0; m < kMT; ++m) {
+    // The reduction buffer is reused per tile: every wave has read the
+    // previous tile's partials before any writes the next one's.
+    if (m > 0) __syncthreads();
+    reduce_store<kOutFp32>(red, acc[m], wave, lane, (mt0 + m) * kTile, (int)blockIdx.x * kTile,
+                           N, C);
+  }
+}
+
+// `groups` workgroup rows of `mt` tiles of A each, from tile m_tile0 on.
+template <bool kOutFp32>
+hipError_t launch_frag_tiles(const uint8_t* a, const uint8_t* as, const uint8_t* b,
+                             const uint8_t* bs, int m_tile0, int groups, int mt, int N, int K,
+                             void* C, hipStream_t stream) {
+  const dim3 grid(N / kTile, groups);
+  switch (mt) {
+    case 1:
+      hipLaunchKernelGGL((gemm_frag_kernel<kOutFp32, 1, 4>), grid, dim3(kThreads), 0, stream, a,
+                         as, b, bs, m_tile0, N, K, C);
+      break;
+    case 2:
+      hipLaunchKernelGGL((gemm_frag_kernel<kOutFp32, 2, 2>), grid, dim3(kThreads), 0, stream, a,
+                         as, b, bs, m_tile0, N, K, C);
+      break;
+    case 3:
+      hipLaunchKernelGGL((gemm_frag_kernel<kOutFp32, 3, 2>), grid, dim3(kThreads), 0, stream, a,
+                         as, b, bs, m_tile0, N, K, C);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -305,20 +354,31 @@ hipError_t launch_gemm_skinny(const void* A, const void* As, const void* B, cons
   return hipGetLastError();
 }
 
+// Tiles of A per workgroup: passes over B are what cost (each pass streams
+// all of B), so the launch uses the fewest groups of at most 3 tiles,
+// ceil(tiles / 3), with sizes as equal as possible: `extra` groups of
+// base + 1 tiles and the rest of base tiles, at most two launches. Measured
+// at N = K = 8192 (B from HBM), M = 64 / 96 / 128 / 160: 10.7 / 13.0 / 19.5 /
+// 23.6 us, against 15.1 / 21.7 / 28.7 / 35.7 us with one tile per
+// workgroup; M = 128 as 3 + 1 tiles took 21.6 us, M = 160 as 2 + 2 + 1 28.3.
 hipError_t launch_gemm_frag(const void* A, const void* As, const void* B, const void* Bs, int M,
                             int N, int K, bool out_fp32, void* C, hipStream_t stream) {
-  const dim3 grid(N / kTile, M / kTile);
   const auto* a = static_cast<const uint8_t*>(A);
   const auto* as = static_cast<const uint8_t*>(As);
   const auto* b = static_cast<const uint8_t*>(B);
   const auto* bs = static_cast<const uint8_t*>(Bs);
-  if (out_fp32)
-    hipLaunchKernelGGL(gemm_frag_kernel<true>, grid, dim3(kThreads), 0, stream, a, as, b, bs, N, K,
-                       C);
-  else
-    hipLaunchKernelGGL(gemm_frag_kernel<false>, grid, dim3(kThreads), 0, stream, a, as, b, bs, N,
-                       K, C);
-  return hipGetLastError();
+  const int tiles_m = M / kTile;
+  const int groups = (tiles_m + kMaxFragTiles - 1) / kMaxFragTiles;
+  const int base = tiles_m / groups, extra = tiles_m % groups;
+  auto launch = [&](int m_tile0, int count, int mt) {
+    return out_fp32 ? launch_frag_tiles<true>(a, as, b, bs, m_tile0, count, mt, N, K, C, stream)
+                    : launch_frag_tiles<false>(a, as, b, bs, m_tile0, count, mt, N, K, C, stream);
+  };
+  if (extra > 0) {
+    const hipError_t e = launch(0, extra, base + 1);
+    if (e != hipSuccess) return e;
+  }
+  return launch(extra * (base + 1), groups - extra, base);
 }
 
 }  // namespace mxfp4

@@ -205,11 +205,13 @@ int mxfp4_gemm_swiglu(const void* A_codes, const void* A_scales, const void* B_c
  *   R % 32 == 0, K % 256 == 0, K <= 2^24, R * K / 2 < 2^40.
  * mxfp4_gemm_frag: mxfp4_gemm with both operands in fragment order (codes
  *   16-byte, scales 4-byte aligned; C as mxfp4_gemm). Built for few rows of
- *   A (decode shapes): one 32 x 32 tile of C per workgroup, the K steps
- *   split between its 8 waves and summed in a fixed order, exactly the
+ *   A (decode shapes): each workgroup takes one 32-row tile of B and up to
+ *   three 32-row tiles of A, the K steps split between its 8 waves and
+ *   summed in a fixed order; every 32 x 32 tile of C gets exactly the
  *   arithmetic of mxfp4_gemm's M <= 128 kernel, so for M <= 128 the two
- *   return identical bits. Requires M % 32 == 0, M / 32 <= 65535,
- *   N % 32 == 0, K % 256 == 0, K <= 2^24, each buffer < 2^40 bytes.
+ *   return identical bits. Requires M % 32 == 0, M <= 6291360 (at most
+ *   65535 groups of three tiles), N % 32 == 0, K % 256 == 0, K <= 2^24,
+ *   each buffer < 2^40 bytes. May enqueue two kernels.
  * All three: asynchronous on `stream`; errors as mxfp4_gemm. */
 int mxfp4_quantize_frag(const void* x_bf16, int64_t M, int64_t K, void* codes_frag,
                         void* scales_frag, void* stream);

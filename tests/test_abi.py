@@ -227,8 +227,9 @@ def test_frag_entries_reject_nulls_and_misalignment():
 
 
 @pytest.mark.parametrize("M,N,K", [(0, 32, 256), (32, 0, 256), (16, 32, 256), (32, 48, 256),
-                                   (32, 32, 128), (32, 32, 1 << 25), (32 * 65536, 32, 256),
-                                   (32 * 65535, 32, 1 << 24)])
+                                   (32, 32, 128), (32, 32, 1 << 25), (1 << 31, 32, 256),
+                                   (32 * 65535, 32, 1 << 24), (1 << 26, 1 << 14, 256),
+                                   (32 * 3 * 65536, 32, 256)])
 def test_gemm_frag_rejects_bad_sizes(M, N, K):
     assert mx.mxfp4_gemm_frag(P16, P16, P16, P16, M, N, K, mx.OUT_BF16, P16, None) == EINVAL
 

@@ -144,10 +144,12 @@ def test_gemm_frag_equals_gemm_and_oracle(M, N, K, out_dtype):
                           c_ref, s_ref)
 
 
-def test_gemm_frag_many_row_tiles():
-    """M = 320 (ten row tiles, past the 128 rows mxfp4_gemm sends to this
-    arithmetic): against the oracle only."""
-    M, N, K = 320, 96, 512
+@pytest.mark.parametrize("M", [160, 224, 320])
+def test_gemm_frag_many_row_tiles(M):
+    """Past the 128 rows mxfp4_gemm sends to this arithmetic, against the
+    oracle only: 5 row tiles run as groups of 3 + 2 (two launches), 7 as
+    3 + 2 + 2, 10 as 3 + 3 + 2 + 2."""
+    N, K = 96, 512
     announce(f"gemm_frag {M}x{N}x{K}")
     ac, as_ = _random_operand(M, K, 21)
     bc, bs = _random_operand(N, K, 22)
