@@ -26,9 +26,13 @@ def _weights(N, K, seed):
     return mx.quantize(w)
 
 
-@pytest.mark.parametrize("path", ["fragment", "tile"])
+# fragment160: 5 row tiles of A, which the fragment-order GEMM enqueues as
+# two kernels (3 + 2 tiles per workgroup); both are captured.
+@pytest.mark.parametrize("path", ["fragment", "fragment160", "tile"])
 def test_captured_step_replays_equal_eager(path):
-    M, N, K = (32, 2048, 4096) if path == "fragment" else (512, 768, 2048)
+    M, N, K = {"fragment": (32, 2048, 4096), "fragment160": (160, 1024, 2048),
+               "tile": (512, 768, 2048)}[path]
+    path = "fragment" if path.startswith("fragment") else path
     announce(f"graph capture, {path} path {M}x{N}x{K}")
     bc, bs = _weights(N, K, 41)
     if path == "fragment":
