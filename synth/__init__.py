@@ -12,6 +12,9 @@ Workloads (shapes and value distributions):
   mlp_gate_up M=16384, N=28672, K=4096, activations N(0,1), weights N(0,0.02)
   mlp_down    M=16384, N=4096, K=14336, same distributions
   ragged      X[4128, 7936] ~ Laplace(0,1), W[6176, 7936] ~ N(0,0.02), FP32 out
+  decode64, decode128
+              the skinny workload's shape and distributions at M = 64 and 128
+              (larger decode batches against the same 8192 x 8192 weight)
 The MLP shapes are those of a Llama-3-8B MLP at 16384 tokens; no weights of
 any trained model are used.
 """
@@ -52,6 +55,10 @@ WORKLOADS = {
                  ("normal", 1.0, 0.0, 1.0), ("normal", 0.02, 0.0, 1.0), 3003, 4003),
         Workload("ragged", 4128, 6176, 7936, OUT_FP32,
                  ("laplace", 1.0), ("normal", 0.02, 0.0, 1.0), 1004, 2004),
+        Workload("decode64", 64, 8192, 8192, OUT_BF16,
+                 ("normal", 1.0, 0.0, 1.0), ("normal", 0.02, 0.0, 1.0), 1005, 2001),
+        Workload("decode128", 128, 8192, 8192, OUT_BF16,
+                 ("normal", 1.0, 0.0, 1.0), ("normal", 0.02, 0.0, 1.0), 1006, 2001),
     ]
 }
 

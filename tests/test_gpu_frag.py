@@ -179,13 +179,14 @@ def test_gemm_frag_output_written_exactly_in_bounds():
     check_gemm_output(buf[pad:-pad].view(M, N), c_ref, s_ref)
 
 
-def test_skinny_workload_full_size_pipeline():
-    """The decode-shaped workload (32 x 8192 x 8192, BF16 out) through the
-    fragment path: activation quantized into fragment order per call, the
-    weight quantized row-major then re-laid out. Equal bit for bit to
-    quantize + mxfp4_gemm on the same inputs, and within tolerance of the
+@pytest.mark.parametrize("name", ["skinny", "decode128"])
+def test_skinny_workload_full_size_pipeline(name):
+    """The decode-shaped workloads (32 or 128 x 8192 x 8192, BF16 out)
+    through the fragment path: activation quantized into fragment order per
+    call, the weight quantized row-major then re-laid out. Equal bit for bit
+    to quantize + mxfp4_gemm on the same inputs, and within tolerance of the
     oracle at sampled outputs."""
-    w = WORKLOADS["skinny"]
+    w = WORKLOADS[name]
     announce(f"fragment pipeline {w.M}x{w.N}x{w.K}")
     a_bits = bf16_matrix((w.M, w.K), w.a_dist, w.a_seed)
     b_bits = bf16_matrix((w.N, w.K), w.b_dist, w.b_seed)
