@@ -1,0 +1,55 @@
+"""Host logic of bench.py (CPU only): the one-GPU refusal and the rule that
+HBM traffic from rocprofv3 counters is reported only for the kernel sources
+it was measured on."""
+
+import json
+import os
+import subprocess
+import sys
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused_before_any_device_work():
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                         capture_output=True, text=True, timeout=120)
+    assert res.returncode == 2
+    assert "one GPU only" in res.stderr
+    assert res.stdout == ""
+
+
+def _entry(tmp_path, sources, sha, nbytes=1234):
+    path = tmp_path / "traffic.json"
+    path.write_text(json.dumps({"workloads": {"square": {
+        "sources": sources, "sha256": sha, "bytes_per_launch": nbytes}}}))
+    return str(path)
+
+
+def test_traffic_reported_only_for_the_measured_sources(tmp_path):
+    src = tmp_path / "k.hip"
+    src.write_text("kernel v1\n")
+    rel = os.path.relpath(src, ROOT)
+    good = bench.source_digest([rel])
+    assert bench.read_traffic(_entry(tmp_path, [rel], good), "square") == 1234
+    # Any change to the sources makes the stored counters stale: null.
+    src.write_text("kernel v2\n")
+    assert bench.read_traffic(_entry(tmp_path, [rel], good), "square") is None
+    # Unknown workload, missing file, malformed file: null.
+    assert bench.read_traffic(_entry(tmp_path, [rel], good), "skinny") is None
+    assert bench.read_traffic(str(tmp_path / "absent.json"), "square") is None
+    bad = tmp_path / "bad.json"
+    bad.write_text("{not json")
+    assert bench.read_traffic(str(bad), "square") is None
+
+
+def test_source_digest_depends_on_every_source_and_their_order(tmp_path):
+    a, b = tmp_path / "a.hip", tmp_path / "b.hip"
+    a.write_text("a\n")
+    b.write_text("b\n")
+    ra, rb = os.path.relpath(a, ROOT), os.path.relpath(b, ROOT)
+    d_ab = bench.source_digest([ra, rb])
+    assert d_ab == bench.source_digest([ra, rb])
+    assert d_ab != bench.source_digest([rb, ra])
+    assert d_ab != bench.source_digest([ra])
