@@ -47,6 +47,34 @@ def build(verbose=True):
     return LIB
 
 
+# A plain C program that drives the library through include/mxfp4.h alone
+# (tests/c_abi/c_abi_check.c), built next to the library by gcc: the C ABI
+# used with no Python in the process.
+C_CHECK_SRC = os.path.join(os.path.dirname(HERE), "tests", "c_abi", "c_abi_check.c")
+C_CHECK_BIN = os.path.join(HERE, "c_abi_check")
+
+
+def c_check_command(out=C_CHECK_BIN, libdir=HERE):
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    return ["gcc", "-std=c11", "-O1", "-Wall", "-Wextra", "-D__HIP_PLATFORM_AMD__",
+            "-I" + os.path.join(rocm, "include"),
+            "-I" + os.path.join(os.path.dirname(HERE), "include"), C_CHECK_SRC,
+            "-L" + libdir, "-L" + os.path.join(rocm, "lib"), "-lmxfp4", "-lamdhip64",
+            "-Wl,-rpath," + libdir, "-Wl,-rpath,$ORIGIN", "-o", str(out)]
+
+
+def build_c_check(out=C_CHECK_BIN, libdir=HERE, verbose=True):
+    """Compile the C ABI check program against libmxfp4.so in `libdir`."""
+    cmd = c_check_command(out, libdir)
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr + "\n")
+        raise subprocess.CalledProcessError(res.returncode, cmd)
+    return str(out)
+
+
 # Host-only AddressSanitizer: the device code is built as usual and the host
 # code (the C ABI's argument checks, launchers, per-device state) is
 # instrumented. Loading the result needs the matching runtime preloaded
@@ -79,3 +107,4 @@ def build_asan(out, verbose=False):
 
 if __name__ == "__main__":
     build()
+    build_c_check()
