@@ -32,7 +32,10 @@ from .stochastic import (  # noqa: F401
     quantize_2d_sr,
 )
 from .swiglu import (  # noqa: F401
+    SILU_ARGMIN,
     silu,
+    silu_range,
+    swiglu_tolerance,
     swiglu_reference,
 )
 from .shuffle import (  # noqa: F401
