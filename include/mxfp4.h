@@ -125,7 +125,16 @@ int mxfp4_quantize_2d_sr(const void* x_bf16, int64_t M, int64_t K, uint64_t seed
  * M <= 128 runs a split-K kernel (one 32 x 32 tile of C per workgroup, the K
  * range split between its waves and summed in LDS in a fixed order); larger
  * M runs 256 x 256 tiles. Both give the same results up to fp32 summation
- * order. */
+ * order.
+ * Accuracy: each 64-wide K slice is one block-scaled MFMA whose sum is added
+ * to an fp32 accumulator with one rounding, so the 256 x 256 kernel takes
+ * K/64 roundings in a row (the split-K kernel K/512 per wave, then 7). With
+ * S = sum_k |dq(a_k) dq(b_k)|, an FP32 result satisfies
+ *   |C - C_exact| <= max(1e-5, (K/64 + 2) * 2^-24) * S,
+ * i.e. 1e-5 * S up to K = 10688 and a bound growing with K past it (about
+ * 6.1e-5 * S at K = 65536); inputs whose first K slices hold a large sum and
+ * whose later slices each add half a unit in its last place reach it. BF16
+ * output is that fp32 value rounded to nearest even. */
 int mxfp4_gemm(const void* A_codes, const void* A_scales, const void* B_codes,
                const void* B_scales, int64_t M, int64_t N, int64_t K, int out_dtype,
                void* C, void* stream);

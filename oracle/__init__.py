@@ -49,6 +49,7 @@ from .frag import (  # noqa: F401
 )
 from .compare import (  # noqa: F401
     FP32_REL_TOL,
+    fp32_rel_tol,
     round_to_bf16,
     bf16_bits_of,
     bf16_ordinal,

@@ -115,3 +115,15 @@ def random_bf16_bits(shape, seed):
     exp_all_ones = (bits & 0x7F80) == 0x7F80
     bits[exp_all_ones] &= 0xBFFF      # inf/NaN patterns -> finite ones
     return bits
+
+
+def large_block_first(rows, K, big_scale):
+    """Packed codes and scales [rows, K/2], [rows, K/32] whose first 256 K
+    hold code 6 (4.0) under scale byte big_scale and every later K code 1
+    (0.5) under big_scale - 8: an input for testing fp32 accumulation with a
+    large partial sum first and many small ones after it."""
+    codes = np.full((rows, K // 2), 0x11, np.uint8)
+    codes[:, :128] = 0x66
+    scales = np.full((rows, K // 32), big_scale - 8, np.uint8)
+    scales[:, :8] = big_scale
+    return codes, scales

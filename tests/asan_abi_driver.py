@@ -61,6 +61,16 @@ def main(path):
         expect(L.mxfp4_gemm(P, P, P, P, M, N, K, 0, P, None), EINVAL, f"gemm {M}x{N}x{K}")
         expect(L.mxfp4_gemm_bshuffled(P, P, P, P, M, N, K, 0, P, None), EINVAL, "bshuffled")
         expect(L.mxfp4_gemm_frag(P, P, P, P, M, N, K, 0, P, None), EINVAL, "frag")
+    # M * N * 4 past int64 (M = N = 2^31 - 32, FP32): rejected, never wrapped.
+    big = (1 << 31) - 32
+    for dt in (0, 1):
+        expect(L.mxfp4_gemm(P, P, P, P, big, big, 256, dt, P, None), EINVAL, "gemm M*N huge")
+        expect(L.mxfp4_gemm_bshuffled(P, P, P, P, big, big, 256, dt, P, None), EINVAL,
+               "bshuffled M*N huge")
+        expect(L.mxfp4_gemm_frag(P, P, P, P, big, big, 256, dt, P, None), EINVAL,
+               "frag M*N huge")
+    expect(L.mxfp4_gemm_swiglu(P, P, P, P, big, (1 << 31) - 256, 256, P, P, None, None), EINVAL,
+           "swiglu M*N huge")
     expect(L.mxfp4_gemm(P, P, P, P, 32, 32, 256, 2, P, None), EINVAL, "gemm dtype")
     expect(L.mxfp4_gemm(None, P, P, P, 32, 32, 256, 0, P, None), EINVAL, "gemm null")
     expect(L.mxfp4_gemm(P + 8, P, P, P, 32, 32, 256, 0, P, None), EALIGN, "gemm align")

@@ -112,6 +112,13 @@ def test_gemm_rejects_oversized_buffers():
     # M * N * 4 bytes >= 2^40
     assert mx.mxfp4_gemm(P16, P16, P16, P16, 1 << 20, 1 << 18, 256, mx.OUT_FP32, P16,
                          None) == EINVAL
+    # M * N * 4 past int64 (M = N = 2^31 - 32): rejected, not wrapped negative.
+    big = (1 << 31) - 32
+    for dt in (mx.OUT_BF16, mx.OUT_FP32):
+        assert mx.mxfp4_gemm(P16, P16, P16, P16, big, big, 256, dt, P16, None) == EINVAL
+        assert mx.mxfp4_gemm_bshuffled(P16, P16, P16, P16, big, big, 256, dt, P16,
+                                       None) == EINVAL
+        assert mx.mxfp4_gemm_frag(P16, P16, P16, P16, big, big, 256, dt, P16, None) == EINVAL
 
 
 def test_gemm_rejects_misaligned():

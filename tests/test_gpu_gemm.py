@@ -23,7 +23,7 @@ import oracle
 from conftest import read_golden
 from gpu_helpers import (DEV, announce, bf16_bits_of_tensor, bf16_to_dev, check_gemm_output,
                          sample_pairs, u8_to_dev)
-from synth import WORKLOADS, bf16_matrix, random_codes, random_scales
+from synth import WORKLOADS, bf16_matrix, large_block_first, random_codes, random_scales
 
 pytestmark = pytest.mark.gpu
 
@@ -242,41 +242,80 @@ def test_side_stream(M):
     check_gemm_output(out, c_ref, s_ref)
 
 
-@pytest.mark.parametrize("name", ["tiny", "skinny", "square", "mlp_gate_up", "mlp_down", "ragged"])
-def test_workload_full_size(name):
-    """The workload end to end at full size: GPU quantize of A and B, GPU GEMM;
-    the oracle quantizes the sampled rows itself and computes the sampled
-    outputs (random pairs plus the bottom-right corner, which holds the
-    ragged tile edges)."""
-    w = WORKLOADS[name]
-    announce(f"workload {name}: {w.M}x{w.N}x{w.K} out={'fp32' if w.out_dtype else 'bf16'}")
+def _workload_operands(w):
     a_bits = bf16_matrix((w.M, w.K), w.a_dist, w.a_seed)
     b_bits = bf16_matrix((w.N, w.K), w.b_dist, w.b_seed)
     ac, as_ = mx.quantize(bf16_to_dev(a_bits))
     bc, bs = mx.quantize(bf16_to_dev(b_bits))
     out_dtype = torch.float32 if w.out_dtype == mx.OUT_FP32 else torch.bfloat16
+    return a_bits, b_bits, ac, as_, bc, bs, out_dtype
+
+
+@pytest.mark.parametrize("name", ["tiny", "skinny", "square", "ragged"])
+def test_workload_full_size(name):
+    """The workload end to end at full size, every output compared: GPU
+    quantize of A and B (bit-exact with the oracle's quantize of all rows),
+    GPU GEMM against the oracle's float64 C and S computed from the oracle's
+    own codes. The square workload also runs the GEMM on pre-shuffled B (the
+    bench step's GEMM), which must give the same bits."""
+    w = WORKLOADS[name]
+    announce(f"workload {name}: {w.M}x{w.N}x{w.K} out={'fp32' if w.out_dtype else 'bf16'}, full C")
+    a_bits, b_bits, ac, as_, bc, bs, out_dtype = _workload_operands(w)
+    out = mx.gemm(ac, as_, bc, bs, out_dtype=out_dtype)
+    shuf = None
+    if name == "square":
+        bsh, bssh = mx.shuffle_b(bc, bs)
+        shuf = mx.gemm_bshuffled(ac, as_, bsh, bssh, w.N, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    ra_c, ra_s = oracle.quantize(a_bits)
+    del a_bits
+    assert np.array_equal(ac.cpu().numpy(), ra_c) and np.array_equal(as_.cpu().numpy(), ra_s)
+    rb_c, rb_s = oracle.quantize(b_bits)
+    del b_bits
+    assert np.array_equal(bc.cpu().numpy(), rb_c) and np.array_equal(bs.cpu().numpy(), rb_s)
+    c_ref, s_ref = oracle.gemm(ra_c, ra_s, rb_c, rb_s)
+    misses = check_gemm_output(out, c_ref, s_ref)
+    print(f"[gpu] {name}: all {w.M * w.N} outputs compared, literal BF16 misses {misses}",
+          flush=True)
+    _assert_not_silent_zeros(out.float().cpu().numpy(), c_ref, s_ref)
+    if shuf is not None:
+        assert torch.equal(out, shuf), "pre-shuffled GEMM differs from mxfp4_gemm"
+
+
+def _tile_class_rows(M, count, seed):
+    """Whole-row sample: rows at every offset class of a 256-row tile (MFMA
+    tile row, lane row), spread over tile rows, plus the first and last."""
+    rng = np.random.default_rng(seed)
+    tiles = rng.integers(0, M // 256, size=count)
+    offs = (32 * (np.arange(count) % 8) + rng.integers(0, 32, size=count))
+    return np.unique(np.concatenate([256 * tiles + offs, [0, M - 1]]))
+
+
+@pytest.mark.parametrize("name", ["mlp_gate_up", "mlp_down"])
+def test_workload_mlp_whole_rows(name):
+    """Llama-MLP shapes at full size: whole rows of C (every column, so every
+    tile column, wave and MFMA column of the kernel) at rows of every offset
+    class within a tile, and the codes of all of B and of those rows of A
+    bit-exact with the oracle's."""
+    w = WORKLOADS[name]
+    announce(f"workload {name}: {w.M}x{w.N}x{w.K} bf16, whole rows")
+    a_bits, b_bits, ac, as_, bc, bs, out_dtype = _workload_operands(w)
     out = mx.gemm(ac, as_, bc, bs, out_dtype=out_dtype)
     torch.cuda.synchronize()
-
-    m_idx, n_idx = sample_pairs(w.M, w.N, 3000, seed=len(name))
-    rows_a = np.unique(m_idx)
-    rows_b = np.unique(n_idx)
-    ra_c, ra_s = oracle.quantize(a_bits[rows_a])
-    rb_c, rb_s = oracle.quantize(b_bits[rows_b])
-    # GPU codes of the sampled rows are the oracle's, bit for bit.
-    ridx_a = torch.from_numpy(rows_a).to(DEV)
-    ridx_b = torch.from_numpy(rows_b).to(DEV)
-    assert np.array_equal(ac[ridx_a].cpu().numpy(), ra_c)
-    assert np.array_equal(as_[ridx_a].cpu().numpy(), ra_s)
-    assert np.array_equal(bc[ridx_b].cpu().numpy(), rb_c)
-    assert np.array_equal(bs[ridx_b].cpu().numpy(), rb_s)
-    # Oracle outputs at the sampled pairs, from the oracle's own codes.
-    pos_a = np.searchsorted(rows_a, m_idx)
-    pos_b = np.searchsorted(rows_b, n_idx)
-    c_ref, s_ref = oracle.gemm_entries(ra_c, ra_s, rb_c, rb_s, pos_a, pos_b)
-    got = out[torch.from_numpy(m_idx).to(DEV), torch.from_numpy(n_idx).to(DEV)]
+    rows = _tile_class_rows(w.M, 40, seed=len(name))
+    ra_c, ra_s = oracle.quantize(a_bits[rows])
+    del a_bits
+    ridx = torch.from_numpy(rows).to(DEV)
+    assert np.array_equal(ac[ridx].cpu().numpy(), ra_c)
+    assert np.array_equal(as_[ridx].cpu().numpy(), ra_s)
+    rb_c, rb_s = oracle.quantize(b_bits)
+    del b_bits
+    assert np.array_equal(bc.cpu().numpy(), rb_c) and np.array_equal(bs.cpu().numpy(), rb_s)
+    c_ref, s_ref = oracle.gemm(ra_c, ra_s, rb_c, rb_s)
+    got = out[ridx]
     misses = check_gemm_output(got, c_ref, s_ref)
-    print(f"[gpu] {name}: {m_idx.size} sampled outputs, literal BF16 misses {misses}", flush=True)
+    print(f"[gpu] {name}: {rows.size} whole rows ({rows.size * w.N} outputs), literal BF16 "
+          f"misses {misses}", flush=True)
     _assert_not_silent_zeros(got.float().cpu().numpy(), c_ref, s_ref)
 
 
@@ -312,3 +351,48 @@ def test_maximum_k_closed_form(M):
         got = mx.gemm_frag(af, asf, bf, bsf, M, N, K, out_dtype=torch.float32)
         torch.cuda.synchronize()
         assert torch.equal(got, want)
+
+
+@pytest.mark.parametrize("K", [8192, 14336, 65536])
+@pytest.mark.parametrize("M", [32, 256])
+def test_fp32_accumulation_worst_case(M, K):
+    """A large partial sum first and half-ulp slices after it: every
+    sequential fp32 rounding loses its slice. The closed form of C is
+    8192 + (K - 256) 2^-17 (all products positive, so S = C); the error must
+    stay within fp32_rel_tol(K) * S on the split-K (M = 32), tile (M = 256)
+    and fragment-order kernels, and within 1e-5 * S up to K = 8192."""
+    N = 64
+    announce(f"fp32 accumulation worst case M={M} K={K}")
+    ac, as_ = large_block_first(M, K, 127)
+    bc, bs = large_block_first(N, K, 128)
+    exact = 8192.0 + (K - 256) * 2.0 ** -17
+    A, As_, B, Bs = (u8_to_dev(t) for t in (ac, as_, bc, bs))
+    outs = {"gemm": mx.gemm(A, As_, B, Bs, out_dtype=torch.float32)}
+    if M <= 128:
+        af, asf = mx.to_frag(A, As_)
+        bf, bsf = mx.to_frag(B, Bs)
+        outs["gemm_frag"] = mx.gemm_frag(af, asf, bf, bsf, M, N, K, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    tol = oracle.fp32_rel_tol(K)
+    for name, out in outs.items():
+        err = np.abs(out.cpu().numpy().astype(np.float64) - exact).max()
+        print(f"[gpu] {name}: max error {err:.6g} = {err / exact:.3e} S (bar {tol:.3e} S)",
+              flush=True)
+        assert err <= tol * exact, name
+        if K <= 8192:
+            assert err <= oracle.FP32_REL_TOL * exact, name
+
+
+@pytest.mark.parametrize("K", [65536, 262144])
+@pytest.mark.parametrize("M", [32, 160])
+def test_fp32_random_operands_long_k(M, K):
+    """Random codes and scales at K far past the workloads' 14336, on both
+    kernels, against the oracle at fp32_rel_tol(K)."""
+    N = 64
+    announce(f"gemm random fp32 {M}x{N}x{K}")
+    Ac, Bc = random_codes(M, K, K + M), random_codes(N, K, K + 1)
+    As, Bs = random_scales(M, K, K + 2), random_scales(N, K, K + 3)
+    out = _gemm(Ac, As, Bc, Bs, torch.float32)
+    c_ref, s_ref = oracle.gemm(Ac, As, Bc, Bs)
+    check_gemm_output(out, c_ref, s_ref, K=K)
+    _assert_not_silent_zeros(out.cpu().numpy(), c_ref, s_ref)

@@ -16,7 +16,7 @@ import torch
 
 import oracle
 from conftest import read_golden, read_golden_table
-from synth import random_codes, random_scales, random_bf16_bits
+from synth import large_block_first, random_codes, random_scales, random_bf16_bits
 
 GRID = [Fraction(0), Fraction(1, 2), Fraction(1), Fraction(3, 2),
         Fraction(2), Fraction(3), Fraction(4), Fraction(6)]
@@ -372,3 +372,13 @@ def test_check_functions_reject_planted_errors():
     lit, rd = oracle.check_bf16(two_up, c_ref, s_ref)
     assert not lit[:3].any()
     assert not rd[0]                           # 100 + 2 steps (0.5 each) >> 1e-5 * 1000 + ulp/2
+
+
+def test_large_block_first_closed_form():
+    """The FP32 worst-case operands of the GPU tests: the oracle's C and S
+    equal the closed form 8192 + (K - 256) 2^-17 (all products positive)."""
+    for K in (256, 512, 2048):
+        ac, as_ = large_block_first(3, K, 127)
+        bc, bs = large_block_first(5, K, 128)
+        c, s = oracle.gemm(ac, as_, bc, bs)
+        assert np.all(c == 8192.0 + (K - 256) * 2.0 ** -17) and np.array_equal(c, s)
