@@ -52,6 +52,14 @@ int check_device() {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// a * b * c < kMaxBytes for non-negative factors, without overflowing: a
+// product past int64 counts as too large.
+bool below_max_bytes(int64_t a, int64_t b, int64_t c = 1) {
+  int64_t ab = 0, abc = 0;
+  if (__builtin_mul_overflow(a, b, &ab) || __builtin_mul_overflow(ab, c, &abc)) return false;
+  return abc < kMaxBytes;
+}
+
 int launch_status(hipError_t e) { return e == hipSuccess ? MXFP4_OK : MXFP4_ELAUNCH; }
 
 }  // namespace
@@ -145,7 +153,8 @@ int mxfp4_gemm(const void* A_codes, const void* A_scales, const void* B_codes,
   if (K % 256 != 0 || M % 32 != 0 || N % 32 != 0 || K > kMaxGemmK) return MXFP4_EINVAL;
   if (out_dtype != MXFP4_OUT_BF16 && out_dtype != MXFP4_OUT_FP32) return MXFP4_EINVAL;
   const int64_t out_bytes = out_dtype == MXFP4_OUT_FP32 ? 4 : 2;
-  if (M * (K / 2) >= kMaxBytes || N * (K / 2) >= kMaxBytes || M * N * out_bytes >= kMaxBytes)
+  if (!below_max_bytes(M, K / 2) || !below_max_bytes(N, K / 2) ||
+      !below_max_bytes(M, N, out_bytes))
     return MXFP4_EINVAL;
   if (!aligned(A_codes, 16) || !aligned(B_codes, 16) || !aligned(A_scales, 4) ||
       !aligned(B_scales, 4) || !aligned(C, 16))
@@ -195,7 +204,7 @@ int mxfp4_gemm_bshuffled(const void* A_codes, const void* A_scales, const void* 
   const int64_t out_bytes = out_dtype == MXFP4_OUT_FP32 ? 4 : 2;
   int64_t cb = 0, sb = 0;
   mxfp4::shuffled_b_sizes(N, K, &cb, &sb);
-  if (M * (K / 2) >= kMaxBytes || cb >= kMaxBytes || M * N * out_bytes >= kMaxBytes)
+  if (!below_max_bytes(M, K / 2) || cb >= kMaxBytes || !below_max_bytes(M, N, out_bytes))
     return MXFP4_EINVAL;
   if (!aligned(A_codes, 16) || !aligned(Bsh_codes, 16) || !aligned(A_scales, 4) ||
       !aligned(Bsh_scales, 4) || !aligned(C, 16))
@@ -217,7 +226,7 @@ int mxfp4_gemm_swiglu(const void* A_codes, const void* A_scales, const void* B_c
     return MXFP4_EINVAL;
   if (K % 256 != 0 || M % 32 != 0 || N % 256 != 0 || K > kMaxGemmK) return MXFP4_EINVAL;
   // The per-lane code offsets of the up half are 32-bit: B's codes < 2 GiB.
-  if (N * (K / 2) >= kMaxSwigluB || M * (K / 2) >= kMaxBytes || M * N >= kMaxBytes)
+  if (N * (K / 2) >= kMaxSwigluB || !below_max_bytes(M, K / 2) || !below_max_bytes(M, N))
     return MXFP4_EINVAL;
   if (!aligned(A_codes, 16) || !aligned(B_codes, 16) || !aligned(A_scales, 4) ||
       !aligned(B_scales, 4) || !aligned(act_codes, 16) ||
@@ -270,7 +279,8 @@ int mxfp4_gemm_frag(const void* A_frag, const void* A_scales_frag, const void* B
   if ((M / 32 + 2) / 3 > 65535) return MXFP4_EINVAL;
   if (out_dtype != MXFP4_OUT_BF16 && out_dtype != MXFP4_OUT_FP32) return MXFP4_EINVAL;
   const int64_t out_bytes = out_dtype == MXFP4_OUT_FP32 ? 4 : 2;
-  if (M * (K / 2) >= kMaxBytes || N * (K / 2) >= kMaxBytes || M * N * out_bytes >= kMaxBytes)
+  if (!below_max_bytes(M, K / 2) || !below_max_bytes(N, K / 2) ||
+      !below_max_bytes(M, N, out_bytes))
     return MXFP4_EINVAL;
   if (!aligned(A_frag, 16) || !aligned(B_frag, 16) || !aligned(A_scales_frag, 4) ||
       !aligned(B_scales_frag, 4) || !aligned(C, 16))
