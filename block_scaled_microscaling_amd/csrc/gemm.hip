@@ -143,6 +143,7 @@ struct Ctx {
   int b_scale_blk;        // pre-shuffled B: first scale block of this tile
   uint32_t lane16;        // 16 * lane
   int klast, hlast;
+  int rot, rot_chunks;    // K rotation of this workgroup's XCD: K steps (multiple of 4), chunks
   uint32_t code_lane[2];  // per-lane code DMA offset for row groups at 16 r, 16 r + 8
   const uint8_t* tile_a;  // wave-uniform code bases of this tile, less kDmaBias
   const uint8_t* tile_b;
@@ -160,6 +161,22 @@ struct Ctx {
   uint32_t s_sel;          // byte-permute selector picking this lane half's bytes
   int wave;
 };
+
+// Logical K step T (and 1024-K scale chunk) -> the step (chunk) loaded: the
+// K loop of every workgroup of one XCD starts rot steps into K and wraps
+// around. Cold operands: the 8 XCDs running tiles of one B panel row then
+// read different parts of it at any moment, so each part comes from HBM for
+// the first XCD only and from the last-level cache for the other seven,
+// instead of all eight waiting on HBM together. rot is 0 unless K % 1024 ==
+// 0, and a multiple of 4 steps, so scale chunks stay whole.
+__device__ __forceinline__ int phys_step(const Ctx& c, int t) {
+  const int p = t + c.rot;
+  return p >= c.ksteps ? p - c.ksteps : p;
+}
+__device__ __forceinline__ int phys_chunk(const Ctx& c, int ch) {
+  const int p = ch + c.rot_chunks;
+  return p >= c.nchunks ? p - c.nchunks : p;
+}
 
 // Global B row of B-tile row t (0..255), clamped into B. With kGlu the tile
 // covers activation columns col0 .. col0 + 127 of a stacked [W_gate; W_up]
@@ -240,7 +257,7 @@ __device__ __forceinline__ void load_scale_part(const Ctx& c, uint8_t* buf, int 
   if constexpr (kShufB && X == 1) {
     // The shuffled scale block is the LDS chunk image: part U of wave w is
     // bytes 1024 U + 256 w + 4 lane of it.
-    const int chunk_c = min(chunk, c.nchunks - 1);
+    const int chunk_c = phys_chunk(c, min(chunk, c.nchunks - 1));
     const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(buf) + kChunkBytes +
                                                         4 * (256 * U + 64 * c.wave));
     dma4(c.Bs + (int64_t)(c.b_scale_blk + chunk_c) * kChunkBytes + 1024 * U + 256 * c.wave +
@@ -252,7 +269,9 @@ __device__ __forceinline__ void load_scale_part(const Ctx& c, uint8_t* buf, int 
   const int t_row = 128 * (U / 4) + 8 * (U % 4) + 2 * c.wave + c.scale_lane;
   const int row = X == 0 ? min(c.row0 + t_row, c.M - 1) : b_row<kGlu>(c, t_row);
   const int t = c.scale_t ^ (4 * (U % 2) + c.wave);
-  const int hs = min(kChunk * chunk + t, c.hlast);
+  // With a rotation every chunk is whole (K % 1024 == 0).
+  const int hs = c.rot ? kChunk * phys_chunk(c, min(chunk, c.nchunks - 1)) + t
+                       : min(kChunk * chunk + t, c.hlast);
   const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(buf) + X * kChunkBytes +
                                                       4 * (256 * U + 64 * c.wave));
   dma4(base + (int64_t)row * c.scale_row_bytes + hs * 4, dst);
@@ -269,7 +288,7 @@ __device__ __forceinline__ void load_scale_pair(const Ctx& c, uint8_t* buf, int 
   const uint8_t* base = X == 0 ? c.As : c.Bs;
   // The last steps prefetch chunks past the end of K: those re-read the last
   // chunk (never used) instead of running past the scale rows.
-  const int chunk_c = min(chunk, c.hlast / kChunk);
+  const int chunk_c = phys_chunk(c, min(chunk, c.hlast / kChunk));
   const uint8_t* sbase;
   if constexpr (kShufB && X == 1) {
     // Parts 2 PP, 2 PP + 1 of wave w: bytes 2048 PP + 256 w (+ 1024) of the
@@ -365,7 +384,7 @@ __device__ __forceinline__ void k_step(const Ctx& c0, Tiles& tl,
   Ctx c = c0;
   asm volatile("" : "+v"(c.scale_lane), "+v"(c.scale_t));
   asm volatile("" : "+v"(c.s_off), "+v"(c.sb_off), "+v"(c.s_x), "+v"(c.s_sel));
-  const int kb = min(T + 1, c.klast);
+  const int kb = phys_step(c, min(T + 1, c.klast));
   // Phase 0: slice 0; read slice 1.
   mma_row<0, 0>(acc, fa, sc0);
   read_frag_b<S>(c, tl, 1, 0, fb.b[0]);
@@ -426,7 +445,7 @@ __device__ __forceinline__ void k_step(const Ctx& c0, Tiles& tl,
   step_barrier();
   MXFP4_FENCE();
   // Phase 3: slice 3; read slice 0 and the scales of step T+1.
-  const int ka = min(T + 2, c.klast);
+  const int ka = phys_step(c, min(T + 2, c.klast));
   const int hs = 2 * (T + 1);
   const uint8_t* sbuf = chunks[(hs / kChunk) & 1];
   const int pchunk = (T + 1) / kChunkSteps + 1;
@@ -465,14 +484,15 @@ __device__ __forceinline__ void issue_tile_head(const Ctx& c0, Tiles& tl,
                                                 uint8_t (*chunks)[2 * kChunkBytes]) {
   Ctx c = c0;
   asm volatile("" : "+v"(c.scale_lane), "+v"(c.scale_t));
-  load_a2<0, 0>(c, tl, 0);
-  load_a2<2, 0>(c, tl, 0);
-  load_a2<4, 0>(c, tl, 0);
-  load_a2<6, 0>(c, tl, 0);
-  load_b2<kShufB, 0, 0>(c, tl, 0);
-  load_b2<kShufB, 2, 0>(c, tl, 0);
-  load_b2<kShufB, 4, 0>(c, tl, 0);
-  load_b2<kShufB, 6, 0>(c, tl, 0);
+  const int k0 = c.rot;
+  load_a2<0, 0>(c, tl, k0);
+  load_a2<2, 0>(c, tl, k0);
+  load_a2<4, 0>(c, tl, k0);
+  load_a2<6, 0>(c, tl, k0);
+  load_b2<kShufB, 0, 0>(c, tl, k0);
+  load_b2<kShufB, 2, 0>(c, tl, k0);
+  load_b2<kShufB, 4, 0>(c, tl, k0);
+  load_b2<kShufB, 6, 0>(c, tl, k0);
   load_scale_part<kGlu, kShufB, 0, 0>(c, chunks[0], 0);
   load_scale_part<kGlu, kShufB, 0, 1>(c, chunks[0], 0);
   load_scale_part<kGlu, kShufB, 0, 2>(c, chunks[0], 0);
@@ -498,8 +518,8 @@ __device__ __forceinline__ void issue_tile_tail(const Ctx& c0, Tiles& tl,
                                                 uint8_t (*chunks)[2 * kChunkBytes]) {
   Ctx c = c0;
   asm volatile("" : "+v"(c.scale_lane), "+v"(c.scale_t));
-  load_a2<0, 1>(c, tl, min(1, c.klast));
-  load_a2<2, 1>(c, tl, min(1, c.klast));
+  load_a2<0, 1>(c, tl, phys_step(c, min(1, c.klast)));
+  load_a2<2, 1>(c, tl, phys_step(c, min(1, c.klast)));
   load_scale_part<kGlu, kShufB, 0, 0>(c, chunks[1], 1);
   load_scale_part<kGlu, kShufB, 1, 0>(c, chunks[1], 1);
   load_scale_part<kGlu, kShufB, 0, 1>(c, chunks[1], 1);
@@ -802,6 +822,8 @@ void gemm_tile_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__
   c.lane16 = 16u * (uint32_t)lane;
   c.klast = ksteps - 1;
   c.hlast = 2 * ksteps - 1;
+  c.rot = kFull ? (((int)(blockIdx.x % kNumXcd) * ksteps) / kNumXcd) & ~3 : 0;
+  c.rot_chunks = c.rot / kChunkSteps;
   c.wave = wave;
 #pragma unroll
   for (int par = 0; par < 2; ++par) {
