@@ -1,27 +1,39 @@
 """Benchmark of the MXFP4 hot path on one MI355X (gfx950).
 
-One step = row-wise BF16 -> MXFP4 quantize of the activation A [M, K] plus the
-block-scaled GEMM C = dq(A) dq(B)^T against pre-quantized weights B [N, K],
-on the square workload M = N = K = 8192 with BF16 output (the headline MXFP4
-GEMM shape). Inputs are seeded synthetic BF16 (N(0,1) with 1% of entries x100)
-resident in HBM before the timed region. Weight preparation (quantize, and
-for the tile kernel the one-time pre-shuffle of B) happens before it; the
-GEMM on B in its plain layout is timed alone beside it.
+Headline step = row-wise BF16 -> MXFP4 quantize of the activation A [M, K]
+(mxfp4_quantize) plus the block-scaled GEMM C = dq(A) dq(B)^T against
+pre-quantized weights B [N, K] in their plain row-major layout (mxfp4_gemm,
+the contract entry point), on the square workload M = N = K = 8192 with BF16
+output. Inputs are seeded synthetic BF16 (N(0,1) with 1% of entries x100)
+resident in HBM before the timed region; weight quantization happens before
+it. The step rotates through several copies of its activation and weights
+(more than twice the 256 MB last-level cache in all), so each step reads its
+operands from HBM.
+
+Order of work: inputs and weights are prepared, then every per-kernel time
+of the headline workload is taken, then W untimed and K timed steps run.
+
+Per-kernel times: each kernel runs at least 50 untimed launches (and at
+least 100 ms) on the launch stream, then 10 groups of 10 back-to-back
+launches, each group between one HIP event pair on that stream; the figure
+is the median of the 10 group means (events between single launches would
+add a few microseconds to each). Launches rotate through operand copies as
+the step does.
 
 Prints one JSON line:
   value        2*M*N*K / (time per step), TFLOP/s, whole step (quantize + GEMM)
-  roofline     the GEMM kernel against the FP4 MFMA dense peak (10.1 PFLOP/s):
-               achieved = 2*M*N*K / mean GEMM launch time; for GEMMs with at
-               most 128 rows of A (skinny) against HBM (8 TB/s): achieved =
-               algorithmic bytes (A, B codes + scales, C) / mean launch time,
-               with B rotated through enough copies that it is read from HBM
-               each launch. Launch times come from back-to-back launches on
-               the launch stream with one HIP event pair around them (events
-               between launches add a few microseconds to each); so does
-               every other per-kernel time in the line. The timed steps have
-               no events inside.
-  cpu_baseline the float64 NumPy oracle on a bounded sample of the same
-               workload (up to an 8192 x 8192 block of C over the full K, the
+  roofline     the step's GEMM kernel against the FP4 MFMA dense peak
+               (10.1 PFLOP/s): achieved = 2*M*N*K / median launch time
+  engine_clock_mhz, socket_power_w  the GFX clock (mean over XCDs) and
+               socket power from amdsmi's GPU metrics, read every 20 ms over
+               300 ms of back-to-back headline GEMM launches (medians), when
+               amdsmi can read them
+  configs      every workload: GEMM time, its roofline (FP4 MFMA peak, or
+               HBM for GEMMs with at most 128 rows of A, whose bytes are
+               mostly B), quantize time and rate of its activation, the
+               faster layout variant, and the oracle's rate on a sample
+  cpu_baseline the float64 NumPy oracle on a bounded sample of the headline
+               workload (an 8192 x 8192 block of C over the full K = the
                whole square GEMM, including the oracle's quantize of the
                operand rows it needs)
 
@@ -35,6 +47,7 @@ import argparse
 import json
 import os
 import sys
+import threading
 import time
 
 import numpy as np
@@ -47,18 +60,24 @@ FP4_DENSE_PEAK_TFLOPS = 10100.0   # MI355X dense MXFP4 MFMA peak
 HBM_PEAK_GBPS = 8000.0
 LLC_BYTES = 256 << 20             # MI355X last-level (Infinity) cache
 HBM_BOUND_MAX_M = 128             # GEMMs with at most this many rows of A stream B
+WARM_LAUNCHES = 50
+WARM_MS = 100.0
+GROUPS = 10
+PER_GROUP = 10
+CONFIG_ORDER = ["tiny", "skinny", "square", "mlp_gate_up", "mlp_down", "ragged"]
+CONFIG_INDEX = {"tiny": "0", "skinny": "1", "square": "2", "mlp_gate_up": "3a",
+                "mlp_down": "3b", "ragged": "4"}
 
 
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
-    # 200 untimed steps (about 60 ms of GPU work): measured, the square GEMM
-    # reads 9% slower after 10 warm-up steps than after 300, while the
-    # engine clock and caches settle.
-    p.add_argument("--warmup", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="square")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-configs", action="store_true",
+                   help="skip the per-workload sweep (headline workload only)")
     p.add_argument("--no-swiglu", action="store_true",
                    help="skip timing the fused SwiGLU gate+up GEMM at the Llama MLP shape")
     p.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "gemm_traffic.json"),
@@ -106,25 +125,99 @@ def copy_calibration(mib):
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}), flush=True)
 
 
-def cpu_baseline(a_bits, b_bits, K, rows=8192, cols=8192):
+def oracle_rate(a_bits, b_bits, K, rows, cols):
+    """Wall time of the float64 oracle on a rows x cols block of C over the
+    full K (quantize of those operand rows, dequantize, C and S matmuls)."""
     import oracle
-    cores = len(os.sched_getaffinity(0))
     rows = min(rows, a_bits.shape[0])
     cols = min(cols, b_bits.shape[0])
     t0 = time.perf_counter()
     ac, as_ = oracle.quantize(a_bits[:rows])
     bc, bs = oracle.quantize(b_bits[:cols])
-    c, _s = oracle.gemm_block(ac, as_, bc, bs)
+    oracle.gemm_block(ac, as_, bc, bs)
     dt = time.perf_counter() - t0
-    flops = 2.0 * rows * cols * K
+    return rows, cols, dt, 2.0 * rows * cols * K / dt / 1e12
+
+
+def cpu_baseline(a_bits, b_bits, K, rows=8192, cols=8192):
+    rows, cols, dt, tflops = oracle_rate(a_bits, b_bits, K, rows, cols)
     return {
-        "value": flops / dt / 1e12,
+        "value": tflops,
         "unit": "TFLOP/s",
-        "cores": cores,
+        "cores": len(os.sched_getaffinity(0)),
         "kind": "oracle",
         "sample": (f"C block {rows}x{cols} over K={K}: oracle quantize of {rows}+{cols} rows, "
                    f"float64 dequantize, C and S matmuls; {dt:.2f} s wall"),
     }
+
+
+def _num(v):
+    """A metric value as a float, or None for 'N/A' and the like."""
+    try:
+        f = float(v)
+    except (TypeError, ValueError):
+        return None
+    return f if 0 < f < 65535 else None
+
+
+class ClockSampler:
+    """Reads the GFX engine clock (MHz: the mean of the per-XCD current
+    clocks in amdsmi's GPU metrics, else its average clock) and the socket
+    power (W) every `period_s` while active; stop() returns the medians, or
+    None where amdsmi cannot read them."""
+
+    def __init__(self, torch, period_s=0.02):
+        self.period_s = period_s
+        self.samples = []
+        self.handle = None
+        self._on = threading.Event()
+        self._stop = threading.Event()
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            idx = torch.cuda._get_amdsmi_device_index(0)
+            self.amdsmi = amdsmi
+            self.handle = amdsmi.amdsmi_get_processor_handles()[idx]
+            self.read()
+        except Exception:  # noqa: BLE001 - any failure means no clock reading
+            self.handle = None
+            return
+        self._thread = threading.Thread(target=self._run, daemon=True)
+        self._thread.start()
+
+    def read(self):
+        m = self.amdsmi.amdsmi_get_gpu_metrics_info(self.handle)
+        clks = [c for c in (_num(v) for v in (m.get("current_gfxclks") or [])) if c]
+        clk = float(np.mean(clks)) if clks else _num(m.get("average_gfxclk_frequency"))
+        power = _num(m.get("current_socket_power")) or _num(m.get("average_socket_power"))
+        return clk, power
+
+    def _run(self):
+        while not self._stop.is_set():
+            if self._on.wait(0.1):
+                try:
+                    self.samples.append(self.read())
+                except Exception:  # noqa: BLE001
+                    pass
+                time.sleep(self.period_s)
+
+    def start(self):
+        self.samples = []
+        self._on.set()
+
+    def stop(self):
+        """(median clock MHz, median power W), each None if unread."""
+        self._on.clear()
+        if self.handle is None:
+            return None, None
+        out = []
+        for k in range(2):
+            vals = [smp[k] for smp in self.samples if smp[k] is not None]
+            out.append(float(np.median(vals)) if vals else None)
+        return tuple(out)
+
+    def close(self):
+        self._stop.set()
 
 
 def make_holder(torch, stream):
@@ -148,55 +241,181 @@ def make_holder(torch, stream):
     return hold
 
 
-def time_swiglu(mx, torch, dev, stream, reps=10):
+def make_timer(torch, mx, stream, hold):
+    """time_kernel(launch, name, short) -> median ms per launch (see the
+    module docstring). short: the kernel is shorter than a host launch, so
+    the GPU is held while the host queues the timed groups."""
+
+    def once(launch, name, i):
+        rc = launch(i)  # a C status from the raw entries; the helpers raise
+        if isinstance(rc, int) and rc != 0:
+            raise mx.Mxfp4Error(rc, name)
+
+    def time_kernel(launch, name, short=False):
+        i = 0
+        t0 = time.perf_counter()
+        while i < WARM_LAUNCHES or (time.perf_counter() - t0) * 1e3 < WARM_MS:
+            once(launch, name, i)
+            i += 1
+            if i % 20 == 0:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(GROUPS)]
+        if short:
+            hold(5.0 + 0.06 * GROUPS * PER_GROUP)
+        for e0, e1 in evs:
+            e0.record(stream)
+            for _ in range(PER_GROUP):
+                once(launch, name, i)
+                i += 1
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return float(np.median([e0.elapsed_time(e1) / PER_GROUP for e0, e1 in evs]))
+
+    return time_kernel
+
+
+MAX_COPIES = 64
+
+
+def copies_for(nbytes):
+    """Operand copies to rotate through so that they cover twice the LLC (at
+    most 64: smaller operand sets stay cache-resident, and say so)."""
+    return min(MAX_COPIES, max(1, -(-2 * LLC_BYTES // max(nbytes, 1))))
+
+
+def is_short(M, N, K):
+    """A GEMM shorter than a host launch (skinny M, or under 0.1 TFLOP):
+    time it with the GPU held while the host queues the launches."""
+    return M <= HBM_BOUND_MAX_M or 2.0 * M * N * K < 1e11
+
+
+def gemm_roofline(M, N, K, out_bytes, ms, traffic=None):
+    flops = 2.0 * M * N * K
+    nbytes = (M + N) * (K // 2 + K // 32) + M * N * out_bytes
+    if M <= HBM_BOUND_MAX_M:
+        gbps = nbytes / (ms * 1e-3) / 1e9
+        return {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": gbps / HBM_PEAK_GBPS, "traffic": traffic}
+    tflops = flops / (ms * 1e-3) / 1e12
+    return {"bound": "mfma", "achieved": tflops, "peak": FP4_DENSE_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": tflops / FP4_DENSE_PEAK_TFLOPS, "traffic": traffic}
+
+
+def to_dev(torch, bits, dev):
+    return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+
+def bench_config(torch, mx, dev, stream, time_kernel, w, oracle_sample=True):
+    """GEMM and activation-quantize times of workload `w` (contract entries,
+    and the faster layout variant: pre-shuffled B for M > 128, fragment order
+    for M <= 128), with operand copies rotated past the LLC."""
+    from synth import bf16_matrix
+    M, N, K = w.M, w.N, w.K
+    print(f"bench: config {CONFIG_INDEX[w.name]} ({w.name}) {M}x{N}x{K}", file=sys.stderr,
+          flush=True)
+    a_bits = bf16_matrix((M, K), w.a_dist, w.a_seed)
+    b_bits = bf16_matrix((N, K), w.b_dist, w.b_seed)
+    x = to_dev(torch, a_bits, dev)
+    bc, bs = mx.quantize(to_dev(torch, b_bits, dev))
+    out_dtype = torch.float32 if w.out_dtype == mx.OUT_FP32 else torch.bfloat16
+    out_bytes = 4 if w.out_dtype == mx.OUT_FP32 else 2
+    op_bytes = (M + N) * (K // 2 + K // 32)
+    n = copies_for(op_bytes)
+    ac, as_ = mx.quantize(x)
+    sets = [(ac, as_, bc, bs)] + [tuple(t.clone() for t in (ac, as_, bc, bs))
+                                  for _ in range(n - 1)]
+    c = torch.empty((M, N), dtype=out_dtype, device=dev)
+    short = is_short(M, N, K)
+
+    def gemm(i):
+        a, a_s, b, b_s = sets[i % n]
+        return mx.mxfp4_gemm(a.data_ptr(), a_s.data_ptr(), b.data_ptr(), b_s.data_ptr(), M, N, K,
+                             w.out_dtype, c.data_ptr(), stream.cuda_stream)
+
+    g_ms = time_kernel(gemm, "mxfp4_gemm", short)
+    xs = [x] + [x.clone() for _ in range(copies_for(M * K * 2) - 1)]
+    qc = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+    qs = torch.empty((M, K // 32), dtype=torch.uint8, device=dev)
+
+    def quant(i):
+        return mx.mxfp4_quantize_async(xs[i % len(xs)].data_ptr(), M, K, qc.data_ptr(),
+                                       qs.data_ptr(), stream.cuda_stream)
+
+    q_ms = time_kernel(quant, "mxfp4_quantize", short)
+    q_bytes = M * K * 2 + M * K // 2 + M * K // 32
+    out = {
+        "shape": f"{M}x{N}x{K}", "out": "fp32" if out_bytes == 4 else "bf16",
+        "gemm_us": g_ms * 1e3,
+        "gemm_roofline": gemm_roofline(M, N, K, out_bytes, g_ms),
+        "quantize_us": q_ms * 1e3,
+        "quantize_gbps": q_bytes / (q_ms * 1e-3) / 1e9,
+        "quantize_hbm_frac": q_bytes / (q_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        "operand_copies_rotated": n,
+        "llc_resident": n * op_bytes < 2 * LLC_BYTES,
+    }
+    if short and M % 32 == 0:
+        frag = [(mx.to_frag(a, a_s), mx.to_frag(b, b_s)) for a, a_s, b, b_s in sets]
+
+        def gemm_f(i):
+            (af, asf), (bf, bsf) = frag[i % n]
+            return mx.mxfp4_gemm_frag(af.data_ptr(), asf.data_ptr(), bf.data_ptr(),
+                                      bsf.data_ptr(), M, N, K, w.out_dtype, c.data_ptr(),
+                                      stream.cuda_stream)
+        v_ms = time_kernel(gemm_f, "mxfp4_gemm_frag", short)
+        out["variant"] = "fragment order (mxfp4_gemm_frag)"
+        del frag
+    else:
+        shuf = [mx.shuffle_b(b, b_s) for _, _, b, b_s in sets]
+
+        def gemm_s(i):
+            a, a_s, _, _ = sets[i % n]
+            bsh, bssh = shuf[i % n]
+            return mx.mxfp4_gemm_bshuffled(a.data_ptr(), a_s.data_ptr(), bsh.data_ptr(),
+                                           bssh.data_ptr(), M, N, K, w.out_dtype, c.data_ptr(),
+                                           stream.cuda_stream)
+        v_ms = time_kernel(gemm_s, "mxfp4_gemm_bshuffled", short)
+        out["variant"] = "pre-shuffled B (mxfp4_gemm_bshuffled)"
+        del shuf
+    out["variant_gemm_us"] = v_ms * 1e3
+    out["variant_gemm_roofline_frac"] = gemm_roofline(M, N, K, out_bytes, v_ms)["frac"]
+    del sets, xs, c
+    if oracle_sample:
+        rows, cols, dt, tflops = oracle_rate(a_bits, b_bits, K, 256, 1024)
+        out["oracle"] = {"tflops": tflops, "sample": f"C block {rows}x{cols} over K={K}",
+                         "sample_s": dt,
+                         "full_gemm_s_at_that_rate": 2.0 * M * N * K / (tflops * 1e12)}
+    return out
+
+
+def time_swiglu(mx, torch, dev, stream, time_kernel):
     """The gate+up GEMM of the Llama-3-8B MLP shape (16384 x 28672 x 4096)
-    with its fused SwiGLU + MXFP4 requantize epilogue, timed alone, beside
-    the plain GEMM of the same shape writing its 940 MB BF16 C."""
+    with its fused SwiGLU + MXFP4 requantize epilogue, beside the plain GEMM
+    of the same shape writing its 940 MB BF16 C."""
     from synth import WORKLOADS, bf16_matrix
     w = WORKLOADS["mlp_gate_up"]
     M, N, K = w.M, w.N, w.K
     print(f"bench: fused SwiGLU gate+up {M}x{N}x{K}", file=sys.stderr, flush=True)
-    a = torch.from_numpy(bf16_matrix((M, K), w.a_dist, w.a_seed).view(np.int16))
-    ac, as_ = mx.quantize(a.view(torch.bfloat16).to(dev))
-    b = torch.from_numpy(bf16_matrix((N, K), w.b_dist, w.b_seed).view(np.int16))
-    bc, bs = mx.quantize(b.view(torch.bfloat16).to(dev))
-    del a, b
+    ac, as_ = mx.quantize(to_dev(torch, bf16_matrix((M, K), w.a_dist, w.a_seed), dev))
+    bc, bs = mx.quantize(to_dev(torch, bf16_matrix((N, K), w.b_dist, w.b_seed), dev))
     Nh = N // 2
     codes = torch.empty((M, Nh // 2), dtype=torch.uint8, device=dev)
     scales = torch.empty((M, Nh // 32), dtype=torch.uint8, device=dev)
     c = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
 
-    def fused():
-        rc = mx.mxfp4_gemm_swiglu(ac.data_ptr(), as_.data_ptr(), bc.data_ptr(), bs.data_ptr(),
-                                  M, N, K, codes.data_ptr(), scales.data_ptr(), None,
-                                  stream.cuda_stream)
-        if rc != 0:
-            raise mx.Mxfp4Error(rc, "mxfp4_gemm_swiglu")
+    def fused(i):
+        return mx.mxfp4_gemm_swiglu(ac.data_ptr(), as_.data_ptr(), bc.data_ptr(), bs.data_ptr(),
+                                    M, N, K, codes.data_ptr(), scales.data_ptr(), None,
+                                    stream.cuda_stream)
 
-    def plain():
-        mx.gemm(ac, as_, bc, bs, out=c)
+    def plain(i):
+        return mx.mxfp4_gemm(ac.data_ptr(), as_.data_ptr(), bc.data_ptr(), bs.data_ptr(), M, N, K,
+                             mx.OUT_BF16, c.data_ptr(), stream.cuda_stream)
 
-    # Both kernels warm up together (the first kernel timed after a cold
-    # start otherwise reads 10-15% slow), then each is timed twice,
-    # alternating, and the two means are averaged.
-    for _ in range(10):
-        fused()
-        plain()
-    torch.cuda.synchronize()
     out = {"shape": f"{M}x{N}x{K}"}
-    times = {"fused": [], "plain_bf16_gemm": []}
-    for _ in range(2):
-        for name, fn in (("fused", fused), ("plain_bf16_gemm", plain)):
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for _ in range(reps):
-                fn()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            times[name].append(e0.elapsed_time(e1) / reps)
-    for name, ts in times.items():
-        ms = float(np.mean(ts))
+    for name, fn in (("fused", fused), ("plain_bf16_gemm", plain)):
+        ms = time_kernel(fn, name)
         out[name + "_ms"] = ms
         out[name + "_tflops"] = 2.0 * M * N * K / (ms * 1e-3) / 1e12
     return out
@@ -223,171 +442,114 @@ def main():
     torch.cuda.set_device(dev)
     if mx.mxfp4_available() != 1:
         raise RuntimeError("libmxfp4: no gfx950 device")
+    stream = torch.cuda.current_stream()
+    hbm_bound = M <= HBM_BOUND_MAX_M
+    short = is_short(M, N, K)
+    hold = make_holder(torch, stream)
+    time_kernel = make_timer(torch, mx, stream, hold)
+    clock = ClockSampler(torch)
 
     print(f"bench: workload {w.name} M={M} N={N} K={K}; generating inputs", file=sys.stderr,
           flush=True)
     a_bits = bf16_matrix((M, K), w.a_dist, w.a_seed)
     b_bits = bf16_matrix((N, K), w.b_dist, w.b_seed)
-    x = torch.from_numpy(a_bits.view(np.int16)).view(torch.bfloat16).to(dev)
-    wts = torch.from_numpy(b_bits.view(np.int16)).view(torch.bfloat16).to(dev)
     out_dtype = torch.float32 if w.out_dtype == mx.OUT_FP32 else torch.bfloat16
+    out_bytes = 4 if w.out_dtype == mx.OUT_FP32 else 2
 
-    # Pre-quantized weights and preallocated buffers: nothing is allocated
-    # inside the timed region.
-    bc, bs = mx.quantize(wts)
-    del wts
-    # A GEMM with few rows of A streams B from HBM; a single B would stay in
-    # the 256 MB last-level cache between steps, so such workloads rotate
-    # through enough copies of B to cover twice that cache.
-    hbm_bound = M <= HBM_BOUND_MAX_M
-    b_bytes = bc.numel() + bs.numel()
-    copies = max(1, -(-2 * LLC_BYTES // b_bytes)) if hbm_bound else 1
-    weights = [(bc, bs)] + [(bc.clone(), bs.clone()) for _ in range(copies - 1)]
-    # Larger GEMMs run on the tile kernel with B pre-shuffled once (part of
-    # the weight preparation, like its quantization). Skinny ones run the
-    # register-ring kernel on fragment-order operands: the weight copies are
-    # re-laid out once, and the activation is quantized straight into
-    # fragment order each step.
-    shuffled = not hbm_bound
-    frag = hbm_bound and M % 32 == 0 and K % 256 == 0
-    if shuffled:
-        bsh = mx.shuffle_b(bc, bs)
-    if frag:
-        weights_f = [mx.to_frag(wb, ws) for wb, ws in weights]
-        af = torch.empty(M * K // 2, dtype=torch.uint8, device=dev)
-        asf = torch.empty(M * K // 32, dtype=torch.uint8, device=dev)
-    ac = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
-    as_ = torch.empty((M, K // 32), dtype=torch.uint8, device=dev)
+    # Copies of the step's inputs, rotated step by step: the activations X
+    # and, separately, the GEMM operands (A's codes and scales, written by the
+    # step's quantize, and the quantized weight B) each cover more than twice
+    # the last-level cache, so every step reads them from HBM.
+    x0 = to_dev(torch, a_bits, dev)
+    bc0, bs0 = mx.quantize(to_dev(torch, b_bits, dev))
+    op_bytes = (M + N) * (K // 2 + K // 32)
+    x_copies = copies_for(M * K * 2)
+    copies = copies_for(op_bytes)
+    xs = [x0] + [x0.clone() for _ in range(x_copies - 1)]
+    ws = [(bc0, bs0)] + [(bc0.clone(), bs0.clone()) for _ in range(copies - 1)]
+    acs = [(torch.empty((M, K // 2), dtype=torch.uint8, device=dev),
+            torch.empty((M, K // 32), dtype=torch.uint8, device=dev)) for _ in range(copies)]
     c = torch.empty((M, N), dtype=out_dtype, device=dev)
-    stream = torch.cuda.current_stream()
+    for i in range(copies):
+        mx.quantize(xs[i % x_copies], *acs[i])
 
-    counter = [0]
+    def gemm_launch(i):
+        (a, a_s), (b, b_s) = acs[i % copies], ws[i % copies]
+        return mx.mxfp4_gemm(a.data_ptr(), a_s.data_ptr(), b.data_ptr(), b_s.data_ptr(), M, N, K,
+                             w.out_dtype, c.data_ptr(), stream.cuda_stream)
 
-    def gemm_step(i):
-        if frag:
-            wf, wsf = weights_f[i % copies]
-            mx.gemm_frag(af, asf, wf, wsf, M, N, K, out=c)
-        elif shuffled:
-            mx.gemm_bshuffled(ac, as_, bsh[0], bsh[1], N, out=c)
-        else:
-            wb, ws = weights[i % copies]
-            mx.gemm(ac, as_, wb, ws, out=c)
+    def quantize_launch(i):
+        a, a_s = acs[i % copies]
+        return mx.mxfp4_quantize_async(xs[i % x_copies].data_ptr(), M, K, a.data_ptr(),
+                                       a_s.data_ptr(), stream.cuda_stream)
 
-    def quantize_step():
-        if frag:
-            mx.quantize_frag(x, af, asf)
-        else:
-            mx.quantize(x, ac, as_)
+    def step(i):
+        quantize_launch(i)
+        gemm_launch(i)
 
-    def step():
-        quantize_step()
-        gemm_step(counter[0])
-        counter[0] += 1
-
-    for _ in range(args.warmup):
-        step()
+    # Per-kernel times of the headline workload (the GEMM's is the roofline),
+    # then the engine clock over 300 ms of back-to-back GEMM launches.
+    g_ms = time_kernel(gemm_launch, "mxfp4_gemm", short)
+    clock.start()
+    t0 = time.perf_counter()
+    i = 0
+    while time.perf_counter() - t0 < 0.3:
+        gemm_launch(i)
+        i += 1
+        if i % 20 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
+    clock_mhz, power_w = clock.stop()
+    q_ms = time_kernel(quantize_launch, "mxfp4_quantize", short)
+    flops = 2.0 * M * N * K
+    q_bytes = M * K * 2 + M * K // 2 + M * K // 32
+    traffic = read_traffic(args.traffic_json, w.name)
+    roofline = gemm_roofline(M, N, K, out_bytes, g_ms, traffic)
 
+    # The quantize widenings on the same activation copies.
+    seed = 0x5EED
+    a_sr, s_sr = acs[0]
+    qsr_ms = time_kernel(lambda i: mx.mxfp4_quantize_sr(
+        xs[i % x_copies].data_ptr(), M, K, seed, a_sr.data_ptr(), s_sr.data_ptr(),
+        stream.cuda_stream), "mxfp4_quantize_sr", short)
+    q2_ms = q2sr_ms = None
+    if M % 32 == 0:
+        q2_out = (torch.empty((M, K // 2), dtype=torch.uint8, device=dev),
+                  torch.empty((M, K // 32), dtype=torch.uint8, device=dev),
+                  torch.empty((K, M // 2), dtype=torch.uint8, device=dev),
+                  torch.empty((K, M // 32), dtype=torch.uint8, device=dev))
+        ptrs = [t.data_ptr() for t in q2_out]
+        q2_ms = time_kernel(lambda i: mx.mxfp4_quantize_2d(
+            xs[i % x_copies].data_ptr(), M, K, *ptrs, stream.cuda_stream), "mxfp4_quantize_2d",
+            short)
+        q2sr_ms = time_kernel(lambda i: mx.mxfp4_quantize_2d_sr(
+            xs[i % x_copies].data_ptr(), M, K, seed, *ptrs, stream.cuda_stream),
+            "mxfp4_quantize_2d_sr", short)
+        del q2_out
+    q2_bytes = 2 * M * K + 2 * (M * K // 2 + M * K // 32)
+
+    # W untimed steps, then K timed steps with nothing between the two events.
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
-    # Skinny steps are shorter than the host's launch time: a spin before
-    # `start` lets the host queue them ahead of the GPU. Not for the large
-    # workloads: there the GPU is the slower side anyway, and an idle spin
-    # before MFMA-heavy work was measured to slow the next 50 steps by 12%
-    # while the clocks readjust.
-    hold = make_holder(torch, stream) if hbm_bound else (lambda ms: None)
-    hold_ms = 2.0 + 0.3 * args.steps if hbm_bound else 0.0
+    hold_ms = 2.0 + 0.3 * args.steps if short else 0.0
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
-    hold(hold_ms)
-    # Nothing but the steps between the two events: events recorded between
-    # launches add a few microseconds of their own to each.
+    if short:
+        hold(hold_ms)
     start.record(stream)
-    for _ in range(args.steps):
-        step()
+    for i in range(args.steps):
+        step(args.warmup + i)
     stop.record(stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
-
-    ms_total = start.elapsed_time(stop)
-    ms_step = ms_total / args.steps
-    flops = 2.0 * M * N * K
-    q_bytes = M * K * 2 + M * K // 2 + M * K // 32
-
-    # Launch times of the step's kernels and of the widenings, each over
-    # back-to-back launches on the launch stream (3 untimed, then `reps`
-    # between one event pair).
-    def time_alone(launch, name, reps=20):
-        def once(i):
-            rc = launch(i)  # a C status from the raw entries; the helpers raise
-            if isinstance(rc, int) and rc != 0:
-                raise mx.Mxfp4Error(rc, name)
-        for i in range(3):
-            once(i)
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        # Long enough for the host to queue every launch first, also under a
-        # profiler, which slows each launch to tens of microseconds.
-        hold(5.0 + 0.06 * reps)
-        e0.record(stream)
-        for i in range(reps):
-            once(i)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / reps
-
-    # The step's GEMM (skinny: B rotated through its copies, so each launch
-    # reads B from HBM) and the step's quantize.
-    reps_gemm = 10 * copies if hbm_bound else 20
-    g_ms = time_alone(gemm_step, "gemm", reps=reps_gemm)
-    q_ms = time_alone(lambda i: quantize_step(), "quantize")
-    gemm_tflops = flops / (g_ms * 1e-3) / 1e12
-    quant_gbps = q_bytes / (q_ms * 1e-3) / 1e9
-
-    # The GEMM on operands in their plain row-major layout, timed alone (for
-    # skinny workloads over the same rotated weight copies), and the
-    # row-major quantize beside the fragment-order one.
-    def plain_gemm(i):
-        wb, ws = weights[i % copies]
-        return mx.mxfp4_gemm(ac.data_ptr(), as_.data_ptr(), wb.data_ptr(), ws.data_ptr(), M, N, K,
-                             w.out_dtype, c.data_ptr(), stream.cuda_stream)
-    mx.quantize(x, ac, as_)
-    gplain_ms = time_alone(plain_gemm, "mxfp4_gemm", reps=reps_gemm)
-    qplain_ms = time_alone(lambda i: mx.quantize(x, ac, as_), "quantize") if frag else q_ms
-
-    seed = 0x5EED
-    qsr_ms = time_alone(lambda i: mx.mxfp4_quantize_sr(x.data_ptr(), M, K, seed, ac.data_ptr(),
-                                                     as_.data_ptr(), stream.cuda_stream),
-                        "mxfp4_quantize_sr")
-    q2_out = (torch.empty((M, K // 2), dtype=torch.uint8, device=dev),
-              torch.empty((M, K // 32), dtype=torch.uint8, device=dev),
-              torch.empty((K, M // 2), dtype=torch.uint8, device=dev),
-              torch.empty((K, M // 32), dtype=torch.uint8, device=dev))
-    q2_ms = q2sr_ms = None
-    if M % 32 == 0:
-        ptrs = [t.data_ptr() for t in q2_out]
-        q2_ms = time_alone(lambda i: mx.mxfp4_quantize_2d(x.data_ptr(), M, K, *ptrs,
-                                                        stream.cuda_stream),
-                           "mxfp4_quantize_2d")
-        q2sr_ms = time_alone(lambda i: mx.mxfp4_quantize_2d_sr(x.data_ptr(), M, K, seed, *ptrs,
-                                                             stream.cuda_stream),
-                             "mxfp4_quantize_2d_sr")
-    q2_bytes = 2 * M * K + 2 * (M * K // 2 + M * K // 32)
+    ms_step = start.elapsed_time(stop) / args.steps
+    del xs, ws, acs, c
 
     def gbps(nbytes, ms):
         return None if ms is None else nbytes / (ms * 1e-3) / 1e9
-
-    traffic = read_traffic(args.traffic_json, w.name)
-    out_bytes = 4 if w.out_dtype == mx.OUT_FP32 else 2
-    gemm_bytes = (M + N) * (K // 2 + K // 32) + M * N * out_bytes
-    gemm_gbps = gemm_bytes / (g_ms * 1e-3) / 1e9
-    if hbm_bound:
-        roofline = {"bound": "hbm", "achieved": gemm_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                    "frac": gemm_gbps / HBM_PEAK_GBPS, "traffic": traffic}
-    else:
-        roofline = {"bound": "mfma", "achieved": gemm_tflops, "peak": FP4_DENSE_PEAK_TFLOPS,
-                    "unit": "TFLOP/s", "frac": gemm_tflops / FP4_DENSE_PEAK_TFLOPS,
-                    "traffic": traffic}
 
     result = {
         "metric": "MXFP4 GEMM TFLOP/s (2MNK) at 8192^3 + % of FP4 MFMA peak; quantize GB/s",
@@ -403,40 +565,39 @@ def main():
         "dtype": "mxfp4",
         "data": "synthetic",
         "config": {
-            "workload": (f"{w.name}: quantize A[{M},{K}] BF16 -> MXFP4"
-                         f"{' (fragment order)' if frag else ''}, then GEMM "
-                         f"{M}x{N}x{K} against pre-quantized"
-                         f"{', pre-shuffled' if shuffled else ''}"
-                         f"{', fragment-order' if frag else ''} B[{N},{K}], "
-                         f"{'fp32' if w.out_dtype else 'bf16'} out"),
+            "workload": (f"{w.name}: quantize A[{M},{K}] BF16 -> MXFP4 (mxfp4_quantize), then "
+                         f"mxfp4_gemm {M}x{N}x{K} against pre-quantized row-major B[{N},{K}], "
+                         f"{'fp32' if out_bytes == 4 else 'bf16'} out; {x_copies} copies of X "
+                         f"and {copies} of the GEMM operands rotated (each set past twice the "
+                         f"256 MiB last-level cache)"),
             "M": M, "N": N, "K": K,
-            "out_dtype": "fp32" if w.out_dtype else "bf16",
+            "out_dtype": "fp32" if out_bytes == 4 else "bf16",
         },
-        "gemm_tflops": gemm_tflops,
-        "gemm_ms": g_ms,
-        "quantize_gbps": quant_gbps,
-        "quantize_ms": q_ms,
-        "quantize_hbm_frac": quant_gbps / HBM_PEAK_GBPS,
-        "gemm_b_layout": ("pre-shuffled" if shuffled else
-                          "fragment order (A and B)" if frag else "plain"),
-        "gemm_plain_b_ms": gplain_ms,
-        "gemm_plain_b_tflops": flops / (gplain_ms * 1e-3) / 1e12,
-        "gemm_plain_b_gbps_algorithmic": gemm_bytes / (gplain_ms * 1e-3) / 1e9,
-        "quantize_row_major_ms": qplain_ms,
-        "quantize_sr_ms": qsr_ms,
-        "quantize_sr_gbps": gbps(q_bytes, qsr_ms),
-        "quantize_2d_ms": q2_ms,
-        "quantize_2d_gbps": gbps(q2_bytes, q2_ms),
-        "quantize_2d_sr_ms": q2sr_ms,
-        "quantize_2d_sr_gbps": gbps(q2_bytes, q2sr_ms),
-        "wall_s_timed": t_wall,
-        "gpu_hold_ms_before_timed": hold_ms,
-        "gemm_gbps_algorithmic": gemm_gbps,
-        "b_copies_rotated": copies,
         "roofline": roofline,
+        "engine_clock_mhz": clock_mhz,
+        "socket_power_w": power_w,
+        "gemm_us": g_ms * 1e3,
+        "gemm_tflops": flops / (g_ms * 1e-3) / 1e12,
+        "quantize_us": q_ms * 1e3,
+        "quantize_gbps": gbps(q_bytes, q_ms),
+        "quantize_hbm_frac": gbps(q_bytes, q_ms) / HBM_PEAK_GBPS,
+        "quantize_sr_gbps": gbps(q_bytes, qsr_ms),
+        "quantize_2d_gbps": gbps(q2_bytes, q2_ms),
+        "quantize_2d_sr_gbps": gbps(q2_bytes, q2sr_ms),
+        "timing": (f"per-kernel: median of {GROUPS} groups of {PER_GROUP} back-to-back launches "
+                   f"after >= {WARM_LAUNCHES} launches and >= {WARM_MS:.0f} ms untimed, taken "
+                   f"before the step warm-up; step: {args.steps} steps between one event pair"),
+        "wall_s_timed": t_wall,
     }
+    if not args.no_configs:
+        result["configs"] = {
+            CONFIG_INDEX[name]: bench_config(torch, mx, dev, stream, time_kernel, WORKLOADS[name],
+                                             oracle_sample=not args.no_cpu_baseline)
+            for name in CONFIG_ORDER
+        }
     if not args.no_swiglu:
-        result["swiglu_gate_up"] = time_swiglu(mx, torch, dev, stream)
+        result["swiglu_gate_up"] = time_swiglu(mx, torch, dev, stream, time_kernel)
+    clock.close()
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(a_bits, b_bits, K)

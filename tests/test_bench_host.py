@@ -53,3 +53,26 @@ def test_source_digest_depends_on_every_source_and_their_order(tmp_path):
     assert d_ab == bench.source_digest([ra, rb])
     assert d_ab != bench.source_digest([rb, ra])
     assert d_ab != bench.source_digest([ra])
+
+
+def test_operand_rotation_covers_twice_the_cache_with_a_cap():
+    llc = bench.LLC_BYTES
+    assert bench.copies_for(3 * llc) == 1
+    assert bench.copies_for(llc // 2) == 4
+    assert bench.copies_for(llc) == 2 and bench.copies_for(llc + 1) == 2
+    assert bench.copies_for((2 * llc) // 3) == 4     # floored: 3 copies fall short
+    assert bench.copies_for(1000) == bench.MAX_COPIES
+    for nbytes in (35_651_584, 71_303_168, 205_520_896):
+        n = bench.copies_for(nbytes)
+        assert n * nbytes >= 2 * llc and (n - 1) * nbytes < 2 * llc
+
+
+def test_roofline_bound_and_short_kernels():
+    r = bench.gemm_roofline(8192, 8192, 8192, 2, 0.2)
+    assert r["bound"] == "mfma" and abs(r["achieved"] - 2 * 8192 ** 3 / 0.2e-3 / 1e12) < 1e-6
+    assert abs(r["frac"] - r["achieved"] / bench.FP4_DENSE_PEAK_TFLOPS) < 1e-12
+    r = bench.gemm_roofline(32, 8192, 8192, 2, 0.008)
+    nbytes = (32 + 8192) * (4096 + 256) + 32 * 8192 * 2
+    assert r["bound"] == "hbm" and abs(r["achieved"] - nbytes / 8e-6 / 1e9) < 1e-6
+    assert bench.is_short(32, 8192, 8192) and bench.is_short(256, 256, 256)
+    assert not bench.is_short(4128, 6176, 7936) and not bench.is_short(8192, 8192, 8192)
