@@ -478,8 +478,9 @@ __device__ __forceinline__ void k_step(const Ctx& c0, Tiles& tl,
 }
 
 // Issue the loads that start a tile: K step 0 and scale chunk 0 into slot 0
-// and chunks[0].
-template <bool kGlu, bool kShufB>
+// and chunks[0]. With whole chunks (kFull) the scale words go as the K
+// loop's DMA pairs, whose per-lane offsets are prepared per tile.
+template <bool kFull, bool kGlu, bool kShufB>
 __device__ __forceinline__ void issue_tile_head(const Ctx& c0, Tiles& tl,
                                                 uint8_t (*chunks)[2 * kChunkBytes]) {
   Ctx c = c0;
@@ -493,37 +494,27 @@ __device__ __forceinline__ void issue_tile_head(const Ctx& c0, Tiles& tl,
   load_b2<kShufB, 2, 0>(c, tl, k0);
   load_b2<kShufB, 4, 0>(c, tl, k0);
   load_b2<kShufB, 6, 0>(c, tl, k0);
-  load_scale_part<kGlu, kShufB, 0, 0>(c, chunks[0], 0);
-  load_scale_part<kGlu, kShufB, 0, 1>(c, chunks[0], 0);
-  load_scale_part<kGlu, kShufB, 0, 2>(c, chunks[0], 0);
-  load_scale_part<kGlu, kShufB, 0, 3>(c, chunks[0], 0);
-  load_scale_part<kGlu, kShufB, 0, 4>(c, chunks[0], 0);
-  load_scale_part<kGlu, kShufB, 0, 5>(c, chunks[0], 0);
-  load_scale_part<kGlu, kShufB, 0, 6>(c, chunks[0], 0);
-  load_scale_part<kGlu, kShufB, 0, 7>(c, chunks[0], 0);
-  load_scale_part<kGlu, kShufB, 1, 0>(c, chunks[0], 0);
-  load_scale_part<kGlu, kShufB, 1, 1>(c, chunks[0], 0);
-  load_scale_part<kGlu, kShufB, 1, 2>(c, chunks[0], 0);
-  load_scale_part<kGlu, kShufB, 1, 3>(c, chunks[0], 0);
-  load_scale_part<kGlu, kShufB, 1, 4>(c, chunks[0], 0);
-  load_scale_part<kGlu, kShufB, 1, 5>(c, chunks[0], 0);
-  load_scale_part<kGlu, kShufB, 1, 6>(c, chunks[0], 0);
-  load_scale_part<kGlu, kShufB, 1, 7>(c, chunks[0], 0);
+  load_scales2<kFull, kGlu, kShufB, 0, 0>(c, chunks[0], 0);
+  load_scales2<kFull, kGlu, kShufB, 0, 1>(c, chunks[0], 0);
+  load_scales2<kFull, kGlu, kShufB, 0, 2>(c, chunks[0], 0);
+  load_scales2<kFull, kGlu, kShufB, 0, 3>(c, chunks[0], 0);
+  load_scales2<kFull, kGlu, kShufB, 1, 0>(c, chunks[0], 0);
+  load_scales2<kFull, kGlu, kShufB, 1, 1>(c, chunks[0], 0);
+  load_scales2<kFull, kGlu, kShufB, 1, 2>(c, chunks[0], 0);
+  load_scales2<kFull, kGlu, kShufB, 1, 3>(c, chunks[0], 0);
 }
 
 // What phase 3 of step "-1" would have issued: A loads 0..3 of step 1 and
 // parts 0, 1 of chunk 1. Exactly 8 loads: the tile's first wait is vmcnt(8).
-template <bool kGlu, bool kShufB>
+template <bool kFull, bool kGlu, bool kShufB>
 __device__ __forceinline__ void issue_tile_tail(const Ctx& c0, Tiles& tl,
                                                 uint8_t (*chunks)[2 * kChunkBytes]) {
   Ctx c = c0;
   asm volatile("" : "+v"(c.scale_lane), "+v"(c.scale_t));
   load_a2<0, 1>(c, tl, phys_step(c, min(1, c.klast)));
   load_a2<2, 1>(c, tl, phys_step(c, min(1, c.klast)));
-  load_scale_part<kGlu, kShufB, 0, 0>(c, chunks[1], 1);
-  load_scale_part<kGlu, kShufB, 1, 0>(c, chunks[1], 1);
-  load_scale_part<kGlu, kShufB, 0, 1>(c, chunks[1], 1);
-  load_scale_part<kGlu, kShufB, 1, 1>(c, chunks[1], 1);
+  load_scales2<kFull, kGlu, kShufB, 0, 0>(c, chunks[1], 1);
+  load_scales2<kFull, kGlu, kShufB, 1, 0>(c, chunks[1], 1);
 }
 
 // Point the context at tile id p (XCD-aware order). A SwiGLU tile spans
@@ -619,8 +610,6 @@ __device__ __forceinline__ void store_tile(const Ctx& c, v16f_t (&acc)[4][4], in
   }
 }
 
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-
 // Read-back half of the BF16 epilogue: lane l copies rows x = 4 k + l / 16
 // (k = 0..15), 16-byte chunk l % 16, of a parked 64-row block to C. With
 // eight rows per iteration the swizzle key x % 16 = 4 (k % 4) + l / 16 and
@@ -703,86 +692,73 @@ __device__ __forceinline__ float silu(float z) {
   return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
 }
 
-// SwiGLU + MXFP4 epilogue. Tiles (i, 2 b) and (i, 2 b + 1) of a wave hold
-// the gate and up sums of the same 32 x 32 block of activations
+// SwiGLU + MXFP4 epilogue through the wave's 16 KiB LDS region, in four
+// rounds of 32 rows (MFMA tile row i). Tiles (i, 2 b) and (i, 2 b + 1) of a
+// wave hold the gate and up sums of the same 32 x 32 block of activations
 // act = silu(g) * u (rows row0 + 128 wy + 32 i + r, columns
-// col0 + 64 wx + 32 b + 8 q + 4 h + t for register 4 q + t). act is rounded
-// to BF16 and quantized exactly as the row-wise quantize kernel does, one
-// MX block per (row, b): lanes r and r + 32 hold the two halves of a row's
-// block, so the block amax and the code bytes cross between them once each
-// (v_permlane32_swap). The amax is taken on the fp32 values and rounded
-// once: rounding to BF16 is monotone, so this is the amax of the BF16
-// values. Codes go to act_codes [M, Nh/2], scale bytes to act_scales
-// [M, Nh/32], and the BF16 act to act_bf16 [M, Nh] when given.
+// col0 + 64 wx + 32 b + 8 q + 4 h + t for register 4 q + t).
+// Pass 1: the fp32 sums of the round leave the accumulation registers one
+// tile at a time for LDS: row r holds 64 gate then 64 up values (512 bytes),
+// its 16-byte chunk k stored at chunk k ^ r, so that the 8 rows of one write
+// fall on distinct banks.
+// Pass 2: lane l takes row (64 n + l) / 8 and columns 8 ((64 n + l) % 8) ..
+// + 7 (n = 0..3): 8 gate and 8 up sums, act in fp32, rounded to BF16, and
+// four lanes holding one MX block of 32 activations quantize it exactly as
+// the row-wise quantize kernel does. Codes go to act_codes [M, Nh/2] (32
+// bytes per row per wave), scale bytes to act_scales [M, Nh/32] and, when
+// act is given, the BF16 rows to act [M, Nh] as whole 128-byte lines.
+// Few values are live at once, so the epilogue adds no register pressure to
+// the kernel.
 __device__ __forceinline__ void store_tile_swiglu(const int row0, const int col0, const int M,
                                                   const int Nh, v16f_t (&acc)[4][4], int wy,
-                                                  int wx, int lane, uint8_t* __restrict__ codes,
+                                                  int wx, int lane, uint8_t* region,
+                                                  uint8_t* __restrict__ codes,
                                                   uint8_t* __restrict__ scales,
                                                   uint16_t* __restrict__ act) {
   int r = lane & 31, h = lane >> 5;
   asm volatile("" : "+v"(r), "+v"(h));
+  const int ncol = col0 + 64 * wx;  // first activation column of the wave
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int m_base = row0 + wy * 128 + i * 32;
-    const int m = m_base + r;
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const int j0 = col0 + 64 * wx + 32 * b;
-      const bool ok = m_base < M && j0 < Nh;
-      const v16f_t g = acc[i][2 * b];
-      const v16f_t u = acc[i][2 * b + 1];
-      float a[16];
-      float amax = 0.0f;
+    for (int jj = 0; jj < 4; ++jj) {
+      v16f_t v = acc[i][jj];
+      asm volatile("" : "+v"(v));
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        a[k] = silu(g[k]) * u[k];
-        amax = fmaxf(amax, fabsf(a[k]));
-      }
-      uint32_t w[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) w[k] = pack_bf16x2(a[2 * k], a[2 * k + 1]);
-      if (act != nullptr && ok) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          *reinterpret_cast<uint2*>(act + (int64_t)m * Nh + j0 + 8 * q + 4 * h) =
-              make_uint2(w[2 * q], w[2 * q + 1]);
-      }
-      // After the swap each lane holds its own value and its partner's
-      // (lane r + 32 for r < 32, r - 32 otherwise) in the two results.
-      const uint32_t mine = __float_as_uint(amax);
-      const auto both = __builtin_amdgcn_permlane32_swap(mine, mine, false, false);
-      const float bmax = fmaxf(__uint_as_float(both[0]), __uint_as_float(both[1]));
-      const uint32_t mx = pack_bf16x2(bmax, 0.0f) & 0x7FFFu;
-      const uint32_t byte = (uint32_t)max((int)(mx >> 7) - 2, 0);
-      const float scale = __uint_as_float(byte << 23);
-      // d[0]: code bytes 4 q' + 2 h + {0, 1} for q' = 0, 1; d[1] for q' = 2, 3.
-      uint32_t d[2];
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        uint32_t x = 0;
-        x = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(x, __builtin_bit_cast(bf16x2_t, w[4 * e]),
-                                                      scale, 0);
-        x = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(
-            x, __builtin_bit_cast(bf16x2_t, w[4 * e + 1]), scale, 1);
-        x = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(
-            x, __builtin_bit_cast(bf16x2_t, w[4 * e + 2]), scale, 2);
-        x = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(
-            x, __builtin_bit_cast(bf16x2_t, w[4 * e + 3]), scale, 3);
-        d[e] = x;
-      }
-      // Lane half h keeps code bytes 8 h .. 8 h + 7 of the block. Swapping
-      // d[0] of the upper lanes with d[1] of the lower ones leaves, in every
-      // lane, the lower lane's word of that byte range in [0] and the upper
-      // lane's in [1].
-      const auto lh = __builtin_amdgcn_permlane32_swap(d[0], d[1], false, false);
-      const uint32_t lo = lh[0], hi = lh[1];
-      if (ok) {
-        *reinterpret_cast<uint2*>(codes + (int64_t)m * (Nh / 2) + j0 / 2 + 8 * h) =
-            make_uint2((lo & 0xFFFFu) | (hi << 16), (lo >> 16) | (hi & 0xFFFF0000u));
-        if (h == 0) scales[(int64_t)m * (Nh / 32) + j0 / 32] = (uint8_t)byte;
+      for (int q = 0; q < 4; ++q) {
+        // Chunk of columns 32 (jj / 2) + 8 q + 4 h of the gate (jj even) or up half.
+        const int chunk = 16 * (jj & 1) + 8 * (jj >> 1) + 2 * q + h;
+        *reinterpret_cast<float4*>(region + r * 512 + 16 * (chunk ^ r)) =
+            make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
       }
       MXFP4_FENCE();
     }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll 1
+    for (int n = 0; n < 4; ++n) {
+      const int item = 64 * n + lane;
+      const int x = item >> 3, cg = item & 7;  // row of the round, 8-column group
+      const uint8_t* rb = region + x * 512;
+      const float4 g0 = *reinterpret_cast<const float4*>(rb + 16 * ((2 * cg) ^ x));
+      const float4 g1 = *reinterpret_cast<const float4*>(rb + 16 * ((2 * cg + 1) ^ x));
+      const float4 u0 = *reinterpret_cast<const float4*>(rb + 16 * ((16 + 2 * cg) ^ x));
+      const float4 u1 = *reinterpret_cast<const float4*>(rb + 16 * ((17 + 2 * cg) ^ x));
+      const u32x4_t w = {pack_bf16x2(silu(g0.x) * u0.x, silu(g0.y) * u0.y),
+                         pack_bf16x2(silu(g0.z) * u0.z, silu(g0.w) * u0.w),
+                         pack_bf16x2(silu(g1.x) * u1.x, silu(g1.y) * u1.y),
+                         pack_bf16x2(silu(g1.z) * u1.z, silu(g1.w) * u1.w)};
+      const uint32_t byte = scale_byte_of(quad_max(block_quarter_absmax(w)));
+      const uint32_t c = encode8(w, __uint_as_float(byte << 23));
+      const int m = row0 + 128 * wy + 32 * i + x;
+      if (m < M) {
+        *reinterpret_cast<uint32_t*>(codes + (int64_t)m * (Nh / 2) + ncol / 2 + 4 * cg) = c;
+        if ((lane & 3) == 0) scales[(int64_t)m * (Nh / 32) + ncol / 32 + (cg >> 2)] = (uint8_t)byte;
+        if (act != nullptr)
+          *reinterpret_cast<u32x4_t*>(act + (int64_t)m * Nh + ncol + 8 * cg) = w;
+      }
+    }
+    // This round's reads are done before the next round overwrites the region.
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   }
 }
 
@@ -851,8 +827,8 @@ void gemm_tile_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__
   // grid is a multiple of 8, so every tile id keeps its workgroup's XCD.
   int p = blockIdx.x;
   set_tile<kGlu, kShufB>(c, p, tiles_m, tiles_n);
-  issue_tile_head<kGlu, kShufB>(c, tl, chunks);
-  issue_tile_tail<kGlu, kShufB>(c, tl, chunks);
+  issue_tile_head<kFull, kGlu, kShufB>(c, tl, chunks);
+  issue_tile_tail<kFull, kGlu, kShufB>(c, tl, chunks);
   // BF16 C: this wave's previous block lay inside C, so its 32 stores went
   // out between the head and the tail loads of this tile.
   bool whole_prev = false;
@@ -897,18 +873,23 @@ void gemm_tile_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__
     // the last 8 loads issued are the ones the next wait leaves outstanding.
     const int pn = p + gridDim.x;
     if constexpr (kGlu) {
-      store_tile_swiglu(c.row0, c.col0, M, Nh, acc, wy, wx, lane, act_codes, act_scales,
-                        static_cast<uint16_t*>(C));
+      // As for BF16 C: the next tile's head loads go first, the activation
+      // is parked in slot 1, and the tail loads wait for every wave's pass 2.
+      const int row0 = c.row0, col0 = c.col0;
       if (pn < total) {
         set_tile<kGlu, kShufB>(c, pn, tiles_m, tiles_n);
-        issue_tile_head<kGlu, kShufB>(c, tl, chunks);
+        issue_tile_head<kFull, kGlu, kShufB>(c, tl, chunks);
       }
+      uint8_t* region = wave < 2 ? tl.a[1] + 16384 * wave : tl.b[1] + 16384 * (wave - 2);
+      store_tile_swiglu(row0, col0, M, Nh, acc, wy, wx, lane, region, act_codes, act_scales,
+                        static_cast<uint16_t*>(C));
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     } else if constexpr (kOutFp32) {
       // This epilogue does not touch LDS: the next tile's loads go first.
       const Ctx cur_tile = c;
       if (pn < total) {
         set_tile<kGlu, kShufB>(c, pn, tiles_m, tiles_n);
-        issue_tile_head<kGlu, kShufB>(c, tl, chunks);
+        issue_tile_head<kFull, kGlu, kShufB>(c, tl, chunks);
       }
       store_tile<true>(cur_tile, acc, wy, wx, r, h, C);
     } else {
@@ -920,13 +901,13 @@ void gemm_tile_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__
       whole_prev = cur_tile.row0 + wy * 128 + 128 <= M && cur_tile.col0 + wx * 128 + 128 <= N;
       if (pn < total) {
         set_tile<kGlu, kShufB>(c, pn, tiles_m, tiles_n);
-        issue_tile_head<kGlu, kShufB>(c, tl, chunks);
+        issue_tile_head<kFull, kGlu, kShufB>(c, tl, chunks);
       }
       uint8_t* region = wave < 2 ? tl.a[1] + 16384 * wave : tl.b[1] + 16384 * (wave - 2);
       store_tile_bf16_lds(cur_tile, acc, wy, wx, lane, region, C);
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     }
-    if (pn < total) issue_tile_tail<kGlu, kShufB>(c, tl, chunks);
+    if (pn < total) issue_tile_tail<kFull, kGlu, kShufB>(c, tl, chunks);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }

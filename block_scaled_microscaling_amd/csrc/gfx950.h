@@ -33,6 +33,61 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
 }
 
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// Row-wise MXFP4 block arithmetic (used by the quantize kernels and the
+// fused SwiGLU epilogue). Four consecutive lanes hold one 32-element block,
+// 16 bytes (8 BF16) each.
+//   * |x| is the BF16 pattern with bit 15 cleared; non-negative floats order
+//     as integers, so the block max is an integer max (packed u16 pairs),
+//     finished across the four lanes with two quad-permute DPP moves.
+//   * The shared exponent floor(log2 amax) - 2 comes from the exponent field:
+//     scale byte = max(E_field(amax) - 2, 0); a zero or subnormal amax gives 0.
+//   * v_cvt_scalef32_pk_fp4_bf16 divides two BF16 values by the scale and
+//     rounds them to E2M1 (nearest even, saturating); the scale operand
+//     carries the UE8M0 byte in its float exponent field.
+__device__ __forceinline__ u16x2_t abs_pair(uint32_t w) {
+  return __builtin_bit_cast(u16x2_t, w & 0x7FFF7FFFu);
+}
+
+__device__ __forceinline__ uint32_t block_quarter_absmax(u32x4_t q) {
+  u16x2_t m = __builtin_elementwise_max(__builtin_elementwise_max(abs_pair(q.x), abs_pair(q.y)),
+                                        __builtin_elementwise_max(abs_pair(q.z), abs_pair(q.w)));
+  return max((uint32_t)m.x, (uint32_t)m.y);
+}
+
+// Max over the four lanes 4i..4i+3 that hold one block.
+__device__ __forceinline__ uint32_t quad_max(uint32_t v) {
+  uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);
+  v = max(v, o);  // quad_perm [1,0,3,2]
+  o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);
+  return max(v, o);  // quad_perm [2,3,0,1]
+}
+
+// Scale byte of a block from its largest |BF16| pattern.
+__device__ __forceinline__ uint32_t scale_byte_of(uint32_t amax) {
+  return (uint32_t)max((int)(amax >> 7) - 2, 0);
+}
+
+// The word is passed by value: a bit cast applied straight to a vector
+// element (q.y) was seen to read element 0 instead.
+__device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(bf16x2_t, w);
+}
+
+// Eight BF16 values (one lane's quarter of a block) -> eight E2M1 codes,
+// element 2i in bits 4i..4i+3 (the low nibble of byte i first).
+__device__ __forceinline__ uint32_t encode8(u32x4_t q, float scale) {
+  const uint32_t w0 = q[0], w1 = q[1], w2 = q[2], w3 = q[3];
+  uint32_t r = 0;
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, as_bf16x2(w0), scale, 0);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, as_bf16x2(w1), scale, 1);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, as_bf16x2(w2), scale, 2);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, as_bf16x2(w3), scale, 3);
+  return r;
+}
+
 // XOR swizzle of the 16-byte chunk index within a 128-byte LDS row: the
 // lanes reading one chunk column of 16 consecutive rows fall on distinct
 // banks (in groups of 8 and of 16).

@@ -11,63 +11,20 @@
 // per load instruction. Each thread keeps kUnroll such loads in flight.
 // The register-resident design follows the row-wise g2r kernel described on
 // NVIDIA/TransformerEngine #3809 (one wide load per block, no staging, no
-// per-element divide); the arithmetic below is gfx950's:
-//   * |x| is the BF16 pattern with bit 15 cleared; non-negative floats order
-//     as integers, so the block max is an integer max (packed u16 pairs),
-//     finished across the four lanes with two quad-permute DPP moves.
-//   * The shared exponent floor(log2 amax) - 2 comes from the exponent field:
-//     scale byte = max(E_field(amax) - 2, 0); a zero or subnormal amax gives 0.
-//   * v_cvt_scalef32_pk_fp4_bf16 divides two BF16 values by the scale and
-//     rounds them to E2M1 (nearest even, saturating); the scale operand
-//     carries the UE8M0 byte in its float exponent field.
+// per-element divide); the block arithmetic (gfx950.h) is gfx950's: integer
+// amax of the |BF16| patterns, the scale byte from its exponent field, and
+// v_cvt_scalef32_pk_fp4_bf16 for the division, rounding and packing.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "gfx950.h"
 #include "kernels.h"
 
 namespace mxfp4 {
 namespace {
 
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-
 constexpr int kThreads = 256;
 constexpr int kUnroll = 4;
-
-__device__ __forceinline__ u16x2_t abs_pair(uint32_t w) {
-  return __builtin_bit_cast(u16x2_t, w & 0x7FFF7FFFu);
-}
-
-__device__ __forceinline__ uint32_t block_quarter_absmax(u32x4_t q) {
-  u16x2_t m = __builtin_elementwise_max(__builtin_elementwise_max(abs_pair(q.x), abs_pair(q.y)),
-                                        __builtin_elementwise_max(abs_pair(q.z), abs_pair(q.w)));
-  return max((uint32_t)m.x, (uint32_t)m.y);
-}
-
-// Max over the four lanes 4i..4i+3 that hold one block.
-__device__ __forceinline__ uint32_t quad_max(uint32_t v) {
-  uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);
-  v = max(v, o);  // quad_perm [1,0,3,2]
-  o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);
-  return max(v, o);  // quad_perm [2,3,0,1]
-}
-
-// The word is passed by value: a bit cast applied straight to a vector
-// element (q.y) was seen to read element 0 instead.
-__device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t w) {
-  return __builtin_bit_cast(bf16x2_t, w);
-}
-
-__device__ __forceinline__ uint32_t encode8(u32x4_t q, float scale) {
-  const uint32_t w0 = q[0], w1 = q[1], w2 = q[2], w3 = q[3];
-  uint32_t r = 0;
-  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, as_bf16x2(w0), scale, 0);
-  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, as_bf16x2(w1), scale, 1);
-  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, as_bf16x2(w2), scale, 2);
-  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, as_bf16x2(w3), scale, 3);
-  return r;
-}
 
 __global__ __launch_bounds__(kThreads) void quantize_kernel(const u32x4_t* __restrict__ x,
                                                             uint32_t* __restrict__ codes,
@@ -89,7 +46,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const u32x4_t* __res
     // All 64 lanes take part in the DPP moves; a block's four lanes are
     // either all in range or all out (nquarters is a multiple of 4).
     const uint32_t amax = quad_max(block_quarter_absmax(v[u]));
-    const uint32_t byte = (uint32_t)max((int)(amax >> 7) - 2, 0);
+    const uint32_t byte = scale_byte_of(amax);
     const uint32_t c = encode8(v[u], __uint_as_float(byte << 23));
     if (q < nquarters) {
       codes[q] = c;
@@ -129,7 +86,7 @@ __global__ __launch_bounds__(kThreads) void quantize_frag_kernel(const uint8_t* 
     const int r = qi >> 5, j = (qi >> 2) & 7, quarter = qi & 3;
     const int lane = r + 32 * (j >> 2), q = j & 3;
     const uint32_t amax = quad_max(block_quarter_absmax(v[u]));
-    const uint32_t byte = (uint32_t)max((int)(amax >> 7) - 2, 0);
+    const uint32_t byte = scale_byte_of(amax);
     cblk[256 * q + 4 * lane + quarter] = encode8(v[u], __uint_as_float(byte << 23));
     if (quarter == 0) sblk[4 * lane + q] = (uint8_t)byte;
   }
