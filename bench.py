@@ -82,6 +82,9 @@ def parse():
                    help="skip timing the fused SwiGLU gate+up GEMM at the Llama MLP shape")
     p.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "gemm_traffic.json"),
                    help="HBM bytes per GEMM launch from rocprofv3 counters, if measured")
+    p.add_argument("--probe", action="store_true",
+                   help="only run the MFMA / LDS microbenchmark (built by build.build_probe) "
+                        "and print its cases as one JSON line")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="only run a plain device copy of this many MiB three times and exit "
                         "(the known-size kernel that scales the FETCH_SIZE/WRITE_SIZE counters)")
@@ -123,6 +126,22 @@ def copy_calibration(mib):
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}), flush=True)
+
+
+def run_probe():
+    """The MFMA / LDS microbenchmark in a child process: the FP4 MFMA issue
+    rate and clock with and without the tile GEMM's LDS fragment reads, and
+    the LDS read bandwidth."""
+    import subprocess
+    exe = os.path.join(ROOT, "block_scaled_microscaling_amd", "mfma_lds_probe")
+    if not os.path.exists(exe):
+        raise RuntimeError(f"{exe} is missing: build it with build.build_probe()")
+    res = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError(f"mfma_lds_probe failed with status {res.returncode}")
+    cases = [json.loads(line) for line in res.stdout.splitlines() if line.startswith("{")]
+    print(json.dumps({"probe": cases}), flush=True)
 
 
 def oracle_rate(a_bits, b_bits, K, rows, cols):
@@ -429,6 +448,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration_mib:
         copy_calibration(args.copy_calibration_mib)
+        return
+    if args.probe:
+        run_probe()
         return
 
     import torch

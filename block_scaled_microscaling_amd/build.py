@@ -75,6 +75,26 @@ def build_c_check(out=C_CHECK_BIN, libdir=HERE, verbose=True):
     return str(out)
 
 
+# The MFMA / LDS microbenchmark (probe/mfma_lds_probe.hip): a standalone
+# executable, built next to the library and run by `python bench.py --probe`.
+PROBE_SRC = os.path.join(HERE, "probe", "mfma_lds_probe.hip")
+PROBE_BIN = os.path.join(HERE, "mfma_lds_probe")
+
+
+def build_probe(out=PROBE_BIN, verbose=True):
+    hipcc = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")
+    cmd = [hipcc, f"--offload-arch={ARCH}", "-O3", "-std=c++17",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-Wno-unused-command-line-argument", "-o", str(out), PROBE_SRC]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr + "\n")
+        raise subprocess.CalledProcessError(res.returncode, cmd)
+    return str(out)
+
+
 # Host-only AddressSanitizer: the device code is built as usual and the host
 # code (the C ABI's argument checks, launchers, per-device state) is
 # instrumented. Loading the result needs the matching runtime preloaded
@@ -108,3 +128,4 @@ def build_asan(out, verbose=False):
 if __name__ == "__main__":
     build()
     build_c_check()
+    build_probe()
