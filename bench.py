@@ -24,10 +24,10 @@ Prints one JSON line:
   value        2*M*N*K / (time per step), TFLOP/s, whole step (quantize + GEMM)
   roofline     the step's GEMM kernel against the FP4 MFMA dense peak
                (10.1 PFLOP/s): achieved = 2*M*N*K / median launch time
-  engine_clock_mhz, socket_power_w  the GFX clock (mean over XCDs) and
-               socket power from amdsmi's GPU metrics, read every 20 ms over
-               300 ms of back-to-back headline GEMM launches (medians), when
-               amdsmi can read them
+  engine_clock_mhz  the shader clock while the headline GEMM runs back to
+               back: a spin kernel counting clock cycles runs beside the
+               GEMM launches on a second stream (cycles / its duration),
+               against the 2400 MHz the peak assumes
   configs      every workload: GEMM time, its roofline (FP4 MFMA peak, or
                HBM for GEMMs with at most 128 rows of A, whose bytes are
                mostly B), quantize time and rate of its activation, the
@@ -47,7 +47,6 @@ import argparse
 import json
 import os
 import sys
-import threading
 import time
 
 import numpy as np
@@ -170,73 +169,31 @@ def cpu_baseline(a_bits, b_bits, K, rows=8192, cols=8192):
     }
 
 
-def _num(v):
-    """A metric value as a float, or None for 'N/A' and the like."""
-    try:
-        f = float(v)
-    except (TypeError, ValueError):
+def clock_under_load(torch, launch, stream, queued=40, cycles=2_000_000):
+    """Engine clock (MHz) while `launch` runs back to back: `queued` launches
+    go on `stream`, then torch's spin kernel, which waits for `cycles` shader
+    clock cycles, runs on a second stream beside them (one wave, no LDS: it
+    fits next to a workgroup of the persistent GEMM). cycles / its duration
+    is the clock the GEMM runs at, after power and thermal throttling. None
+    if the spin could not start while the launches ran (its duration then
+    includes the wait)."""
+    side = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    for i in range(queued):
+        launch(i)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(side):
+        e0.record(side)
+        torch.cuda._sleep(cycles)
+        e1.record(side)
+    done = torch.cuda.Event(enable_timing=True)
+    done.record(stream)
+    torch.cuda.synchronize()
+    spin_ms = e0.elapsed_time(e1)
+    if e1.elapsed_time(done) <= 0:  # the spin ended after the launches: not beside them
         return None
-    return f if 0 < f < 65535 else None
-
-
-class ClockSampler:
-    """Reads the GFX engine clock (MHz: the mean of the per-XCD current
-    clocks in amdsmi's GPU metrics, else its average clock) and the socket
-    power (W) every `period_s` while active; stop() returns the medians, or
-    None where amdsmi cannot read them."""
-
-    def __init__(self, torch, period_s=0.02):
-        self.period_s = period_s
-        self.samples = []
-        self.handle = None
-        self._on = threading.Event()
-        self._stop = threading.Event()
-        try:
-            import amdsmi
-            amdsmi.amdsmi_init()
-            idx = torch.cuda._get_amdsmi_device_index(0)
-            self.amdsmi = amdsmi
-            self.handle = amdsmi.amdsmi_get_processor_handles()[idx]
-            self.read()
-        except Exception:  # noqa: BLE001 - any failure means no clock reading
-            self.handle = None
-            return
-        self._thread = threading.Thread(target=self._run, daemon=True)
-        self._thread.start()
-
-    def read(self):
-        m = self.amdsmi.amdsmi_get_gpu_metrics_info(self.handle)
-        clks = [c for c in (_num(v) for v in (m.get("current_gfxclks") or [])) if c]
-        clk = float(np.mean(clks)) if clks else _num(m.get("average_gfxclk_frequency"))
-        power = _num(m.get("current_socket_power")) or _num(m.get("average_socket_power"))
-        return clk, power
-
-    def _run(self):
-        while not self._stop.is_set():
-            if self._on.wait(0.1):
-                try:
-                    self.samples.append(self.read())
-                except Exception:  # noqa: BLE001
-                    pass
-                time.sleep(self.period_s)
-
-    def start(self):
-        self.samples = []
-        self._on.set()
-
-    def stop(self):
-        """(median clock MHz, median power W), each None if unread."""
-        self._on.clear()
-        if self.handle is None:
-            return None, None
-        out = []
-        for k in range(2):
-            vals = [smp[k] for smp in self.samples if smp[k] is not None]
-            out.append(float(np.median(vals)) if vals else None)
-        return tuple(out)
-
-    def close(self):
-        self._stop.set()
+    return cycles / (spin_ms * 1e3)
 
 
 def make_holder(torch, stream):
@@ -411,28 +368,34 @@ def bench_config(torch, mx, dev, stream, time_kernel, w, oracle_sample=True):
 def time_swiglu(mx, torch, dev, stream, time_kernel):
     """The gate+up GEMM of the Llama-3-8B MLP shape (16384 x 28672 x 4096)
     with its fused SwiGLU + MXFP4 requantize epilogue, beside the plain GEMM
-    of the same shape writing its 940 MB BF16 C."""
+    of the same shape writing its 940 MB BF16 C, over the same operand
+    copies (rotated past the LLC)."""
     from synth import WORKLOADS, bf16_matrix
     w = WORKLOADS["mlp_gate_up"]
     M, N, K = w.M, w.N, w.K
     print(f"bench: fused SwiGLU gate+up {M}x{N}x{K}", file=sys.stderr, flush=True)
     ac, as_ = mx.quantize(to_dev(torch, bf16_matrix((M, K), w.a_dist, w.a_seed), dev))
     bc, bs = mx.quantize(to_dev(torch, bf16_matrix((N, K), w.b_dist, w.b_seed), dev))
+    n = copies_for((M + N) * (K // 2 + K // 32))
+    sets = [(ac, as_, bc, bs)] + [tuple(t.clone() for t in (ac, as_, bc, bs))
+                                  for _ in range(n - 1)]
     Nh = N // 2
     codes = torch.empty((M, Nh // 2), dtype=torch.uint8, device=dev)
     scales = torch.empty((M, Nh // 32), dtype=torch.uint8, device=dev)
     c = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
 
     def fused(i):
-        return mx.mxfp4_gemm_swiglu(ac.data_ptr(), as_.data_ptr(), bc.data_ptr(), bs.data_ptr(),
+        a, a_s, b, b_s = sets[i % n]
+        return mx.mxfp4_gemm_swiglu(a.data_ptr(), a_s.data_ptr(), b.data_ptr(), b_s.data_ptr(),
                                     M, N, K, codes.data_ptr(), scales.data_ptr(), None,
                                     stream.cuda_stream)
 
     def plain(i):
-        return mx.mxfp4_gemm(ac.data_ptr(), as_.data_ptr(), bc.data_ptr(), bs.data_ptr(), M, N, K,
+        a, a_s, b, b_s = sets[i % n]
+        return mx.mxfp4_gemm(a.data_ptr(), a_s.data_ptr(), b.data_ptr(), b_s.data_ptr(), M, N, K,
                              mx.OUT_BF16, c.data_ptr(), stream.cuda_stream)
 
-    out = {"shape": f"{M}x{N}x{K}"}
+    out = {"shape": f"{M}x{N}x{K}", "operand_copies_rotated": n}
     for name, fn in (("fused", fused), ("plain_bf16_gemm", plain)):
         ms = time_kernel(fn, name)
         out[name + "_ms"] = ms
@@ -469,7 +432,6 @@ def main():
     short = is_short(M, N, K)
     hold = make_holder(torch, stream)
     time_kernel = make_timer(torch, mx, stream, hold)
-    clock = ClockSampler(torch)
 
     print(f"bench: workload {w.name} M={M} N={N} K={K}; generating inputs", file=sys.stderr,
           flush=True)
@@ -510,18 +472,9 @@ def main():
         gemm_launch(i)
 
     # Per-kernel times of the headline workload (the GEMM's is the roofline),
-    # then the engine clock over 300 ms of back-to-back GEMM launches.
+    # and the engine clock the GEMM runs at.
     g_ms = time_kernel(gemm_launch, "mxfp4_gemm", short)
-    clock.start()
-    t0 = time.perf_counter()
-    i = 0
-    while time.perf_counter() - t0 < 0.3:
-        gemm_launch(i)
-        i += 1
-        if i % 20 == 0:
-            torch.cuda.synchronize()
-    torch.cuda.synchronize()
-    clock_mhz, power_w = clock.stop()
+    clock_mhz = None if short else clock_under_load(torch, gemm_launch, stream)
     q_ms = time_kernel(quantize_launch, "mxfp4_quantize", short)
     flops = 2.0 * M * N * K
     q_bytes = M * K * 2 + M * K // 2 + M * K // 32
@@ -597,7 +550,7 @@ def main():
         },
         "roofline": roofline,
         "engine_clock_mhz": clock_mhz,
-        "socket_power_w": power_w,
+        "engine_clock_peak_mhz": 2400,
         "gemm_us": g_ms * 1e3,
         "gemm_tflops": flops / (g_ms * 1e-3) / 1e12,
         "quantize_us": q_ms * 1e3,
@@ -619,7 +572,6 @@ def main():
         }
     if not args.no_swiglu:
         result["swiglu_gate_up"] = time_swiglu(mx, torch, dev, stream, time_kernel)
-    clock.close()
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(a_bits, b_bits, K)
