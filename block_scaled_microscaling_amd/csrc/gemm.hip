@@ -611,17 +611,23 @@ __device__ __forceinline__ void store_tile(const Ctx& c, v16f_t (&acc)[4][4], in
 }
 
 // Read-back half of the BF16 epilogue: lane l copies rows x = 4 k + l / 16
-// (k = 0..15), 16-byte chunk l % 16, of a parked 64-row block to C. With
-// eight rows per iteration the swizzle key x % 16 = 4 (k % 4) + l / 16 and
-// the half swap (k / 4) % 2 are constants, so each read is one of four
-// per-lane bases plus an immediate. Rows at or past rows_left, and lanes
-// whose columns lie past N (n_ok false), store nothing.
-__device__ __forceinline__ void copy_parked_rows(const uint8_t* region, int lane, uint8_t* cptr,
-                                                 int64_t row4_bytes, bool n_ok, int rows_left) {
+// (k = 0..15), 16-byte chunk l % 16, of a parked 64-row block to C, four
+// reads in flight. With four rows per read the swizzle key
+// x % 16 = 4 (k % 4) + l / 16 and the half swap (k / 4) % 2 are constants,
+// so each read is one of four per-lane bases plus an immediate. Each store
+// is a buffer store without a branch: its resource starts at the first of
+// its four rows and covers them (8 N <= 2^31 bytes), lane l's offset is
+// (l / 16) 2 N + 16 (l % 16), and a lane whose row lies at or past rows_left
+// or whose columns lie past N (n_ok false) gets offset 2^31, past the
+// resource, so the hardware drops its store.
+__device__ __forceinline__ void copy_parked_rows(const uint8_t* region, int lane, uint8_t* cbase,
+                                                 int N, bool n_ok, int rows_left) {
   const int l4 = lane >> 4, cc = lane & 15;
   const uint8_t* rb[4];
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) rb[kk] = region + l4 * 256 + (((cc ^ l4) << 4) ^ (64 * kk));
+  const uint32_t row4 = 8u * (uint32_t)N;
+  const uint32_t lane_off = n_ok ? (uint32_t)(l4 * 2 * N + 16 * cc) : 0x80000000u;
 #pragma unroll 1
   for (int g2 = 0; g2 < 2; ++g2) {
 #pragma unroll
@@ -636,10 +642,12 @@ __device__ __forceinline__ void copy_parked_rows(const uint8_t* region, int lane
         uint4 x = w[k];
         if (e) x = make_uint4(x.z, x.w, x.x, x.y);
         const u32x4_t o = {x.x, x.y, x.z, x.w};
+        const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+            cbase + (int64_t)kr * row4, 0, (int)row4, kBufferWord3);
+        const uint32_t voff = 4 * kr + l4 < rows_left ? lane_off : 0x80000000u;
         // Whole lines, written once: stream them past L2 (8% faster when C
         // is large, as in a 16384 x 28672 GEMM).
-        if (n_ok && 4 * kr + l4 < rows_left)
-          __builtin_nontemporal_store(o, reinterpret_cast<u32x4_t*>(cptr + kr * row4_bytes));
+        __builtin_amdgcn_raw_buffer_store_b128(o, rsrc, (int)voff, 0, kBufferNt);
       }
     }
   }
@@ -662,8 +670,8 @@ __device__ __forceinline__ void store_tile_bf16_lds(const Ctx& c, v16f_t (&acc)[
   const int half = 8 * (h ^ ((r >> 4) & 1));
   const int mrow = c.row0 + wy * 128;  // first row and column of the wave's block
   const int ncol = c.col0 + wx * 128;
-  const int l4 = lane >> 4, cc = lane & 15;
-  uint8_t* cptr = static_cast<uint8_t*>(C) + ((int64_t)(mrow + l4) * c.N + ncol + 8 * cc) * 2;
+  const int cc = lane & 15;
+  uint8_t* cbase = static_cast<uint8_t*>(C) + ((int64_t)mrow * c.N + ncol) * 2;
   const int64_t row4_bytes = (int64_t)c.N * 8;
 #pragma unroll
   for (int rd = 0; rd < 2; ++rd) {
@@ -682,7 +690,7 @@ __device__ __forceinline__ void store_tile_bf16_lds(const Ctx& c, v16f_t (&acc)[
         MXFP4_FENCE();
       }
     }
-    copy_parked_rows(region, lane, cptr + 16 * rd * row4_bytes, row4_bytes, ncol + 8 * cc < c.N,
+    copy_parked_rows(region, lane, cbase + 16 * rd * row4_bytes, c.N, ncol + 8 * cc < c.N,
                      c.M - mrow - 64 * rd);
     MXFP4_FENCE();
   }
@@ -829,15 +837,20 @@ void gemm_tile_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__
   set_tile<kGlu, kShufB>(c, p, tiles_m, tiles_n);
   issue_tile_head<kFull, kGlu, kShufB>(c, tl, chunks);
   issue_tile_tail<kFull, kGlu, kShufB>(c, tl, chunks);
-  // BF16 C: this wave's previous block lay inside C, so its 32 stores went
-  // out between the head and the tail loads of this tile.
+  // This wave's previous block lay inside C, so all its stores (32 for
+  // BF16, 64 for FP32) went out between the head and the tail loads of this
+  // tile.
   bool whole_prev = false;
   for (; p < total; p += gridDim.x) {
     // Wait for the head loads (vector memory operations complete in issue
     // order): outstanding may remain the 8 tail loads and, after a whole
-    // BF16 block, the 32 stores issued between head and tail.
+    // block, the stores issued between head and tail. The counter holds at
+    // most 63, so after an FP32 block the oldest 9 of its 64 stores are
+    // waited for too.
     if (kEpi == kEpiBf16 && whole_prev)
       asm volatile("s_waitcnt vmcnt(40)\n\ts_barrier" ::: "memory");
+    else if (kOutFp32 && whole_prev)
+      asm volatile("s_waitcnt vmcnt(63)\n\ts_barrier" ::: "memory");
     else
       asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
 
@@ -887,6 +900,7 @@ void gemm_tile_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__
     } else if constexpr (kOutFp32) {
       // This epilogue does not touch LDS: the next tile's loads go first.
       const Ctx cur_tile = c;
+      whole_prev = cur_tile.row0 + wy * 128 + 128 <= M && cur_tile.col0 + wx * 128 + 128 <= N;
       if (pn < total) {
         set_tile<kGlu, kShufB>(c, pn, tiles_m, tiles_n);
         issue_tile_head<kFull, kGlu, kShufB>(c, tl, chunks);

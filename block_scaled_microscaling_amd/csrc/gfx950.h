@@ -36,6 +36,13 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
+// Buffer resources for raw (untyped, stride 0) buffer stores: word 3 sets
+// the data format to 32 bits, which raw accesses need to be valid; an access
+// whose offset lies at or past the resource's byte count is dropped by the
+// hardware. Cache-policy bits of a buffer instruction: nt (stream past L2).
+constexpr int kBufferWord3 = 0x00020000;
+constexpr int kBufferNt = 2;
+
 // Row-wise MXFP4 block arithmetic (used by the quantize kernels and the
 // fused SwiGLU epilogue). Four consecutive lanes hold one 32-element block,
 // 16 bytes (8 BF16) each.
