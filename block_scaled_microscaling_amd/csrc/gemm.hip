@@ -160,6 +160,7 @@ struct Ctx {
   int s_x;                 // half-step XOR key of the lane's scale rows: (r >> 1) & 7
   uint32_t s_sel;          // byte-permute selector picking this lane half's bytes
   int wave;
+  bool interior;           // off_a, off_b, soff hold the offsets of a tile with no clamped row
 };
 
 // Logical K step T (and 1024-K scale chunk) -> the step (chunk) loaded: the
@@ -227,7 +228,7 @@ __device__ __forceinline__ void dma_pair(const uint8_t* base, uint32_t off0, uin
       "s_mov_b32 m0, %3\n\ts_nop 0\n\t"
       "global_load_lds_dwordx4 %0, %2 offset:%4\n\t"
       "global_load_lds_dwordx4 %1, %2 offset:%5"
-      :: "v"(off0), "v"(off1), "s"(base), "s"(m0), "n"((Q0 % 4) * 1024),
+      :: "v"(off0), "v"(off1), "s"(sgpr_ptr(base)), "s"(m0), "n"((Q0 % 4) * 1024),
          "n"(((Q0 + 1) % 4) * 1024)
       : "m0");
 }
@@ -306,7 +307,7 @@ __device__ __forceinline__ void load_scale_pair(const Ctx& c, uint8_t* buf, int 
       "s_mov_b32 m0, %3\n\ts_nop 0\n\t"
       "global_load_lds_dword %0, %2\n\t"
       "global_load_lds_dword %1, %2 offset:1024"
-      :: "v"(c.soff[X][PP][0]), "v"(c.soff[X][PP][1]), "s"(sbase), "s"(m0)
+      :: "v"(c.soff[X][PP][0]), "v"(c.soff[X][PP][1]), "s"(sgpr_ptr(sbase)), "s"(m0)
       : "m0");
 }
 
@@ -537,6 +538,12 @@ __device__ __forceinline__ void set_tile(Ctx& c, int p, int tiles_m, int tiles_n
   } else {
     c.tile_b = c.B + (int64_t)rb * c.row_bytes - kDmaBias;
   }
+  // The per-lane offsets below are relative to the wave's first rows, so
+  // they are the same for every tile that lies wholly inside A and B (no
+  // clamped row): keep them when both this tile and the last are such.
+  const bool interior = c.row0 + kTileM <= c.M && (kGlu || c.col0 + kTileN <= c.N);
+  if (interior && c.interior) return;
+  c.interior = interior;
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
     const int ga = min(c.row0 + 64 * c.wave + 8 * q, c.M - 8) - ra;
@@ -809,6 +816,7 @@ void gemm_tile_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__
   c.rot = kFull ? (((int)(blockIdx.x % kNumXcd) * ksteps) / kNumXcd) & ~3 : 0;
   c.rot_chunks = c.rot / kChunkSteps;
   c.wave = wave;
+  c.interior = false;
 #pragma unroll
   for (int par = 0; par < 2; ++par) {
     const int prow = lane >> 3;

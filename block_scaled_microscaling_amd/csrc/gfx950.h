@@ -36,6 +36,16 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
+// A pointer the caller knows to be the same in every lane, read from lane 0
+// into scalar registers (an inline-asm "s" operand must not be left to a
+// divergence analysis that cannot see the value is uniform).
+__device__ __forceinline__ const uint8_t* sgpr_ptr(const uint8_t* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<const uint8_t*>((uint64_t)hi << 32 | lo);
+}
+
 // Buffer resources for raw (untyped, stride 0) buffer stores: word 3 sets
 // the data format to 32 bits, which raw accesses need to be valid; an access
 // whose offset lies at or past the resource's byte count is dropped by the
