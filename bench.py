@@ -283,7 +283,7 @@ def to_dev(torch, bits, dev):
     return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
 
 
-def bench_config(torch, mx, dev, stream, time_kernel, w, oracle_sample=True):
+def bench_config(torch, mx, dev, stream, time_kernel, w, oracle_sample=True, traffic=None):
     """GEMM and activation-quantize times of workload `w` (contract entries,
     and the faster layout variant: pre-shuffled B for M > 128, fragment order
     for M <= 128), with operand copies rotated past the LLC."""
@@ -324,7 +324,7 @@ def bench_config(torch, mx, dev, stream, time_kernel, w, oracle_sample=True):
     out = {
         "shape": f"{M}x{N}x{K}", "out": "fp32" if out_bytes == 4 else "bf16",
         "gemm_us": g_ms * 1e3,
-        "gemm_roofline": gemm_roofline(M, N, K, out_bytes, g_ms),
+        "gemm_roofline": gemm_roofline(M, N, K, out_bytes, g_ms, traffic),
         "quantize_us": q_ms * 1e3,
         "quantize_gbps": q_bytes / (q_ms * 1e-3) / 1e9,
         "quantize_hbm_frac": q_bytes / (q_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
@@ -567,7 +567,8 @@ def main():
     if not args.no_configs:
         result["configs"] = {
             CONFIG_INDEX[name]: bench_config(torch, mx, dev, stream, time_kernel, WORKLOADS[name],
-                                             oracle_sample=not args.no_cpu_baseline)
+                                             oracle_sample=not args.no_cpu_baseline,
+                                             traffic=read_traffic(args.traffic_json, name))
             for name in CONFIG_ORDER
         }
     if not args.no_swiglu:
