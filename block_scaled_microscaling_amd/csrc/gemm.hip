@@ -703,27 +703,30 @@ __device__ __forceinline__ void store_tile_bf16_lds(const Ctx& c, v16f_t (&acc)[
   }
 }
 
+// SwiGLU + MXFP4 epilogue through the wave's 16 KiB LDS region. Tiles
+// (i, 2 b) and (i, 2 b + 1) of a wave hold the gate and up sums of the same
+// 32 x 32 block of activations act = silu(g) * u (rows
+// row0 + 128 wy + 32 i + r, columns col0 + 64 wx + 32 b + 8 q + 4 h + t for
+// register 4 q + t), lane for lane.
+// Pass 1: act in fp32 straight from the accumulators, one tile pair at a
+// time, rounded to BF16 and parked: the wave's 128 x 64 BF16 block, row R
+// at 128 R, 16-byte chunk k (columns 8 k .. 8 k + 7) at chunk
+// k ^ ((R >> 1) & 7), so that the 8-byte writes of 32 rows and the 16-byte
+// reads of 8 rows both spread over all banks.
+// Pass 2: item n of lane l is row (64 n + l) / 8 and columns
+// 8 ((64 n + l) % 8) .. + 7: four lanes holding one MX block of 32
+// activations quantize it exactly as the row-wise quantize kernel does.
+// Codes go to act_codes [M, Nh/2] (32 bytes per row per wave), scale bytes
+// to act_scales [M, Nh/32] and, when act is given, the BF16 rows to
+// act [M, Nh] (16 bytes per lane, whole 128-byte lines per 8 lanes).
+__device__ __forceinline__ uint32_t swiglu_park_offset(int R, int k) {
+  return (uint32_t)(128 * R + 16 * (k ^ ((R >> 1) & 7)));
+}
+
 __device__ __forceinline__ float silu(float z) {
   return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
 }
 
-// SwiGLU + MXFP4 epilogue through the wave's 16 KiB LDS region, in four
-// rounds of 32 rows (MFMA tile row i). Tiles (i, 2 b) and (i, 2 b + 1) of a
-// wave hold the gate and up sums of the same 32 x 32 block of activations
-// act = silu(g) * u (rows row0 + 128 wy + 32 i + r, columns
-// col0 + 64 wx + 32 b + 8 q + 4 h + t for register 4 q + t).
-// Pass 1: the fp32 sums of the round leave the accumulation registers one
-// tile at a time for LDS: row r holds 64 gate then 64 up values (512 bytes),
-// its 16-byte chunk k stored at chunk k ^ r, so that the 8 rows of one write
-// fall on distinct banks.
-// Pass 2: lane l takes row (64 n + l) / 8 and columns 8 ((64 n + l) % 8) ..
-// + 7 (n = 0..3): 8 gate and 8 up sums, act in fp32, rounded to BF16, and
-// four lanes holding one MX block of 32 activations quantize it exactly as
-// the row-wise quantize kernel does. Codes go to act_codes [M, Nh/2] (32
-// bytes per row per wave), scale bytes to act_scales [M, Nh/32] and, when
-// act is given, the BF16 rows to act [M, Nh] as whole 128-byte lines.
-// Few values are live at once, so the epilogue adds no register pressure to
-// the kernel.
 __device__ __forceinline__ void store_tile_swiglu(const int row0, const int col0, const int M,
                                                   const int Nh, v16f_t (&acc)[4][4], int wy,
                                                   int wx, int lane, uint8_t* region,
@@ -736,44 +739,45 @@ __device__ __forceinline__ void store_tile_swiglu(const int row0, const int col0
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      v16f_t v = acc[i][jj];
-      asm volatile("" : "+v"(v));
+    for (int b = 0; b < 2; ++b) {
+      v16f_t g = acc[i][2 * b];
+      v16f_t u = acc[i][2 * b + 1];
+      asm volatile("" : "+v"(g), "+v"(u));
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        // Chunk of columns 32 (jj / 2) + 8 q + 4 h of the gate (jj even) or up half.
-        const int chunk = 16 * (jj & 1) + 8 * (jj >> 1) + 2 * q + h;
-        *reinterpret_cast<float4*>(region + r * 512 + 16 * (chunk ^ r)) =
-            make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+        const uint2 w = make_uint2(pack_bf16x2(silu(g[4 * q]) * u[4 * q],
+                                               silu(g[4 * q + 1]) * u[4 * q + 1]),
+                                   pack_bf16x2(silu(g[4 * q + 2]) * u[4 * q + 2],
+                                               silu(g[4 * q + 3]) * u[4 * q + 3]));
+        *reinterpret_cast<uint2*>(region + swiglu_park_offset(32 * i + r, 4 * b + q) + 8 * h) = w;
       }
       MXFP4_FENCE();
     }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  const int mrow = row0 + 128 * wy;
 #pragma unroll 1
-    for (int n = 0; n < 4; ++n) {
-      const int item = 64 * n + lane;
-      const int x = item >> 3, cg = item & 7;  // row of the round, 8-column group
-      const uint8_t* rb = region + x * 512;
-      const float4 g0 = *reinterpret_cast<const float4*>(rb + 16 * ((2 * cg) ^ x));
-      const float4 g1 = *reinterpret_cast<const float4*>(rb + 16 * ((2 * cg + 1) ^ x));
-      const float4 u0 = *reinterpret_cast<const float4*>(rb + 16 * ((16 + 2 * cg) ^ x));
-      const float4 u1 = *reinterpret_cast<const float4*>(rb + 16 * ((17 + 2 * cg) ^ x));
-      const u32x4_t w = {pack_bf16x2(silu(g0.x) * u0.x, silu(g0.y) * u0.y),
-                         pack_bf16x2(silu(g0.z) * u0.z, silu(g0.w) * u0.w),
-                         pack_bf16x2(silu(g1.x) * u1.x, silu(g1.y) * u1.y),
-                         pack_bf16x2(silu(g1.z) * u1.z, silu(g1.w) * u1.w)};
-      const uint32_t byte = scale_byte_of(quad_max(block_quarter_absmax(w)));
-      const uint32_t c = encode8(w, __uint_as_float(byte << 23));
-      const int m = row0 + 128 * wy + 32 * i + x;
+  for (int n0 = 0; n0 < 16; n0 += 4) {
+    u32x4_t w[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int item = 64 * (n0 + k) + lane;
+      w[k] = *reinterpret_cast<const u32x4_t*>(region + swiglu_park_offset(item >> 3, item & 7));
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int item = 64 * (n0 + k) + lane;
+      const int R = item >> 3, cg = item & 7;
+      const uint32_t byte = scale_byte_of(quad_max(block_quarter_absmax(w[k])));
+      const uint32_t c = encode8(w[k], __uint_as_float(byte << 23));
+      const int m = mrow + R;
       if (m < M) {
         *reinterpret_cast<uint32_t*>(codes + (int64_t)m * (Nh / 2) + ncol / 2 + 4 * cg) = c;
         if ((lane & 3) == 0) scales[(int64_t)m * (Nh / 32) + ncol / 32 + (cg >> 2)] = (uint8_t)byte;
         if (act != nullptr)
-          *reinterpret_cast<u32x4_t*>(act + (int64_t)m * Nh + ncol + 8 * cg) = w;
+          *reinterpret_cast<u32x4_t*>(act + (int64_t)m * Nh + ncol + 8 * cg) = w[k];
       }
     }
-    // This round's reads are done before the next round overwrites the region.
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   }
 }
 
