@@ -24,10 +24,9 @@ Prints one JSON line:
   value        2*M*N*K / (time per step), TFLOP/s, whole step (quantize + GEMM)
   roofline     the step's GEMM kernel against the FP4 MFMA dense peak
                (10.1 PFLOP/s): achieved = 2*M*N*K / median launch time
-  engine_clock_mhz  the shader clock while the headline GEMM runs back to
-               back: a spin kernel counting clock cycles runs beside the
-               GEMM launches on a second stream (cycles / its duration),
-               against the 2400 MHz the peak assumes
+  profiled_mfma  the headline GEMM's engine clock and MFMA utilisation as
+               rocprofv3's counters measured them (quoted from the committed
+               profile), against the 2400 MHz the peak assumes
   configs      every workload: GEMM time, its roofline (FP4 MFMA peak, or
                HBM for GEMMs with at most 128 rows of A, whose bytes are
                mostly B), quantize time and rate of its activation, the
@@ -169,31 +168,24 @@ def cpu_baseline(a_bits, b_bits, K, rows=8192, cols=8192):
     }
 
 
-def clock_under_load(torch, launch, stream, queued=40, cycles=2_000_000):
-    """Engine clock (MHz) while `launch` runs back to back: `queued` launches
-    go on `stream`, then torch's spin kernel, which waits for `cycles` shader
-    clock cycles, runs on a second stream beside them (one wave, no LDS: it
-    fits next to a workgroup of the persistent GEMM). cycles / its duration
-    is the clock the GEMM runs at, after power and thermal throttling. None
-    if the spin could not start while the launches ran (its duration then
-    includes the wait)."""
-    side = torch.cuda.Stream()
-    torch.cuda.synchronize()
-    for i in range(queued):
-        launch(i)
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    with torch.cuda.stream(side):
-        e0.record(side)
-        torch.cuda._sleep(cycles)
-        e1.record(side)
-    done = torch.cuda.Event(enable_timing=True)
-    done.record(stream)
-    torch.cuda.synchronize()
-    spin_ms = e0.elapsed_time(e1)
-    if e1.elapsed_time(done) <= 0:  # the spin ended after the launches: not beside them
+def profiled_mfma(kernel="gemm_tile_kernel<0, true, false>", shape="8192^3, BF16"):
+    """Engine clock and MFMA utilisation of the headline GEMM as rocprofv3's
+    counters measured them (profiles/gemm_mfma_utilisation_counters.md, the
+    row of this kernel and shape), or None. A clock read beside the running
+    GEMM from a spin kernel's cycle counter disagreed with the counters
+    (2.34-2.41 against 1.78 GHz), so the line quotes the counters instead."""
+    path = os.path.join(ROOT, "profiles", "gemm_mfma_utilisation_counters.md")
+    try:
+        with open(path) as f:
+            for line in f:
+                cells = [c.strip() for c in line.strip().strip("|").split("|")]
+                if len(cells) >= 7 and cells[0] == f"`mxfp4::{kernel}`" and cells[1] == shape:
+                    return {"clock_ghz": float(cells[5].split()[0]),
+                            "mfma_busy": float(cells[6].rstrip("%")) / 100.0,
+                            "source": "profiles/gemm_mfma_utilisation_counters.md"}
+    except (OSError, ValueError, IndexError):
         return None
-    return cycles / (spin_ms * 1e3)
+    return None
 
 
 def make_holder(torch, stream):
@@ -474,7 +466,6 @@ def main():
     # Per-kernel times of the headline workload (the GEMM's is the roofline),
     # and the engine clock the GEMM runs at.
     g_ms = time_kernel(gemm_launch, "mxfp4_gemm", short)
-    clock_mhz = None if short else clock_under_load(torch, gemm_launch, stream)
     q_ms = time_kernel(quantize_launch, "mxfp4_quantize", short)
     flops = 2.0 * M * N * K
     q_bytes = M * K * 2 + M * K // 2 + M * K // 32
@@ -549,7 +540,7 @@ def main():
             "out_dtype": "fp32" if out_bytes == 4 else "bf16",
         },
         "roofline": roofline,
-        "engine_clock_mhz": clock_mhz,
+        "profiled_mfma": profiled_mfma() if w.name == "square" else None,
         "engine_clock_peak_mhz": 2400,
         "gemm_us": g_ms * 1e3,
         "gemm_tflops": flops / (g_ms * 1e-3) / 1e12,

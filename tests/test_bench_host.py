@@ -76,3 +76,12 @@ def test_roofline_bound_and_short_kernels():
     assert r["bound"] == "hbm" and abs(r["achieved"] - nbytes / 8e-6 / 1e9) < 1e-6
     assert bench.is_short(32, 8192, 8192) and bench.is_short(256, 256, 256)
     assert not bench.is_short(4128, 6176, 7936) and not bench.is_short(8192, 8192, 8192)
+
+
+def test_profiled_mfma_quotes_the_counter_profile():
+    got = bench.profiled_mfma()
+    assert got is not None, "the headline GEMM's row is missing from the MFMA profile"
+    assert 0.5 < got["clock_ghz"] < 2.5
+    assert 0.0 < got["mfma_busy"] <= 1.0
+    assert got["source"] == "profiles/gemm_mfma_utilisation_counters.md"
+    assert bench.profiled_mfma(kernel="no_such_kernel") is None
