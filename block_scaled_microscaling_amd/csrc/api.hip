@@ -22,7 +22,7 @@ namespace {
 
 constexpr int kMaxDevices = 64;
 constexpr int64_t kMaxDim = 2147483647;      // 2^31 - 1
-constexpr int64_t kMaxBf16N = 1LL << 28;     // BF16 C: four rows of C span <= 2^31 bytes
+constexpr int64_t kMaxGemmN = 1LL << 28;     // C: the tile epilogue's store resource spans <= 2^31 bytes
 constexpr int64_t kMaxBytes = int64_t(1) << 40;
 constexpr int64_t kMaxGemmK = int64_t(1) << 24;  // per-lane row offsets of the GEMM kernels are 32-bit
 constexpr int64_t kMaxSwigluB = int64_t(1) << 31;
@@ -153,7 +153,7 @@ int mxfp4_gemm(const void* A_codes, const void* A_scales, const void* B_codes,
     return MXFP4_EINVAL;
   if (K % 256 != 0 || M % 32 != 0 || N % 32 != 0 || K > kMaxGemmK) return MXFP4_EINVAL;
   if (out_dtype != MXFP4_OUT_BF16 && out_dtype != MXFP4_OUT_FP32) return MXFP4_EINVAL;
-  if (out_dtype == MXFP4_OUT_BF16 && N > kMaxBf16N) return MXFP4_EINVAL;
+  if (N > kMaxGemmN) return MXFP4_EINVAL;
   const int64_t out_bytes = out_dtype == MXFP4_OUT_FP32 ? 4 : 2;
   if (!below_max_bytes(M, K / 2) || !below_max_bytes(N, K / 2) ||
       !below_max_bytes(M, N, out_bytes))
@@ -203,7 +203,7 @@ int mxfp4_gemm_bshuffled(const void* A_codes, const void* A_scales, const void* 
     return MXFP4_EINVAL;
   if (K % 256 != 0 || M % 32 != 0 || N % 32 != 0 || K > kMaxGemmK) return MXFP4_EINVAL;
   if (out_dtype != MXFP4_OUT_BF16 && out_dtype != MXFP4_OUT_FP32) return MXFP4_EINVAL;
-  if (out_dtype == MXFP4_OUT_BF16 && N > kMaxBf16N) return MXFP4_EINVAL;
+  if (N > kMaxGemmN) return MXFP4_EINVAL;
   const int64_t out_bytes = out_dtype == MXFP4_OUT_FP32 ? 4 : 2;
   int64_t cb = 0, sb = 0;
   mxfp4::shuffled_b_sizes(N, K, &cb, &sb);
@@ -281,7 +281,7 @@ int mxfp4_gemm_frag(const void* A_frag, const void* A_scales_frag, const void* B
   // (groups of tiles) is at most 65535.
   if ((M / 32 + 2) / 3 > 65535) return MXFP4_EINVAL;
   if (out_dtype != MXFP4_OUT_BF16 && out_dtype != MXFP4_OUT_FP32) return MXFP4_EINVAL;
-  if (out_dtype == MXFP4_OUT_BF16 && N > kMaxBf16N) return MXFP4_EINVAL;
+  if (N > kMaxGemmN) return MXFP4_EINVAL;
   const int64_t out_bytes = out_dtype == MXFP4_OUT_FP32 ? 4 : 2;
   if (!below_max_bytes(M, K / 2) || !below_max_bytes(N, K / 2) ||
       !below_max_bytes(M, N, out_bytes))

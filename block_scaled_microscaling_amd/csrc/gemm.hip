@@ -579,44 +579,6 @@ __device__ __forceinline__ void set_tile(Ctx& c, int p, int tiles_m, int tiles_n
   }
 }
 
-// FP32 (or BF16) epilogue straight from the accumulators.
-template <bool kOutFp32>
-__device__ __forceinline__ void store_tile(const Ctx& c, v16f_t (&acc)[4][4], int wy, int wx,
-                                           int r, int h, void* __restrict__ C) {
-  asm volatile("" : "+v"(r), "+v"(h));
-  // Accumulator register 4q + t of tile (i, j) holds
-  // C[row0 + 128 wy + 32 i + r][col0 + 128 wx + 32 j + 8 q + 4 h + t].
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int m_base = c.row0 + wy * 128 + i * 32;
-    if (m_base >= c.M) continue;
-    const int m = m_base + r;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int n_base = c.col0 + wx * 128 + j * 32;
-      if (n_base >= c.N) continue;
-      v16f_t v = acc[i][j];
-      // Copy this tile out of the accumulator registers here, not all 16
-      // tiles at once at the loop exit.
-      asm volatile("" : "+v"(v));
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int n = n_base + 8 * q + 4 * h;
-        if constexpr (kOutFp32) {
-          float* dst = static_cast<float*>(C) + (int64_t)m * c.N + n;
-          *reinterpret_cast<float4*>(dst) =
-              make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
-        } else {
-          uint16_t* dst = static_cast<uint16_t*>(C) + (int64_t)m * c.N + n;
-          *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(v[4 * q], v[4 * q + 1]),
-                                                      pack_bf16x2(v[4 * q + 2], v[4 * q + 3]));
-        }
-      }
-      MXFP4_FENCE();
-    }
-  }
-}
-
 // Read-back half of the BF16 epilogue: lane l copies rows x = 4 k + l / 16
 // (k = 0..15), 16-byte chunk l % 16, of a parked 64-row block to C, four
 // reads in flight. With four rows per read the swizzle key
@@ -721,6 +683,68 @@ __device__ __forceinline__ void store_tile_bf16_lds(const Ctx& c, v16f_t (&acc)[
 // act [M, Nh] (16 bytes per lane, whole 128-byte lines per 8 lanes).
 __device__ __forceinline__ uint32_t swiglu_park_offset(int R, int k) {
   return (uint32_t)(128 * R + 16 * (k ^ ((R >> 1) & 7)));
+}
+
+// FP32 epilogue through LDS, in four rounds of 32 rows (MFMA tile row i):
+// each wave parks its 32 x 128 fp32 block in its 16 KiB region (512-byte
+// rows; 16-byte chunk c = 8 j + 2 q + h of row r, i.e. columns
+// 32 j + 8 q + 4 h .. + 3, at chunk c ^ (r % 16), so that the writes of 16
+// rows and the reads of one row spread over all banks), then copies it out
+// with 32 lanes per 512-byte row segment: two rows, 8 whole cache lines per
+// store instruction, against 32 partial lines per instruction stored
+// straight from the accumulators. Stores are buffer stores as in
+// copy_parked_rows: one resource per two rows of C (8 N <= 2^31 bytes), a
+// masked lane's offset 2^31 past it. A wave issues exactly 64 stores.
+__device__ __forceinline__ void store_tile_f32_lds(const Ctx& c, v16f_t (&acc)[4][4], int wy,
+                                                   int wx, int lane, uint8_t* region,
+                                                   void* __restrict__ C) {
+  int r = lane & 31, h = lane >> 5;
+  asm volatile("" : "+v"(r), "+v"(h));
+  const int mrow = c.row0 + wy * 128;  // first row and column of the wave's block
+  const int ncol = c.col0 + wx * 128;
+  const int k = lane & 31, x1 = lane >> 5;  // read-back: chunk k of row 2 g + x1
+  const uint32_t row2 = 8u * (uint32_t)c.N;
+  const uint32_t lane_off = ncol + 32 * (k >> 3) < c.N ? x1 * 4u * (uint32_t)c.N + 16u * k
+                                                         : 0x80000000u;
+  uint8_t* cbase = static_cast<uint8_t*>(C) + ((int64_t)mrow * c.N + ncol) * 4;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v16f_t v = acc[i][j];
+      asm volatile("" : "+v"(v));
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int chunk = 8 * j + 2 * q + h;
+        *reinterpret_cast<float4*>(region + r * 512 + 16 * (chunk ^ (r & 15))) =
+            make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+      }
+      MXFP4_FENCE();
+    }
+    const int rows_left = c.M - mrow - 32 * i;
+    uint8_t* rbase = cbase + (int64_t)(32 * i) * c.N * 4;
+#pragma unroll 1
+    for (int g0 = 0; g0 < 16; g0 += 4) {
+      uint4 w[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int x = 2 * (g0 + e) + x1;
+        w[e] = *reinterpret_cast<const uint4*>(region + x * 512 + 16 * (k ^ (x & 15)));
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int g = g0 + e;
+        const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+            rbase + (int64_t)g * row2, 0, (int)row2, kBufferWord3);
+        const uint32_t voff = 2 * g + x1 < rows_left ? lane_off : 0x80000000u;
+        const u32x4_t o = {w[e].x, w[e].y, w[e].z, w[e].w};
+        __builtin_amdgcn_raw_buffer_store_b128(o, rsrc, (int)voff, 0, 0);
+      }
+    }
+    // This round's reads are done before the next round overwrites the region.
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    MXFP4_FENCE();
+  }
 }
 
 __device__ __forceinline__ float silu(float z) {
@@ -849,14 +873,14 @@ void gemm_tile_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__
   set_tile<kGlu, kShufB>(c, p, tiles_m, tiles_n);
   issue_tile_head<kFull, kGlu, kShufB>(c, tl, chunks);
   issue_tile_tail<kFull, kGlu, kShufB>(c, tl, chunks);
-  // This wave's previous block lay inside C, so all its stores (32 for
-  // BF16, 64 for FP32) went out between the head and the tail loads of this
-  // tile.
+  // A previous tile's epilogue issued all its stores (32 for BF16, 64 for
+  // FP32, masked lanes dropped by the store resource) between the head and
+  // the tail loads of this tile.
   bool whole_prev = false;
   for (; p < total; p += gridDim.x) {
     // Wait for the head loads (vector memory operations complete in issue
-    // order): outstanding may remain the 8 tail loads and, after a whole
-    // block, the stores issued between head and tail. The counter holds at
+    // order): outstanding may remain the 8 tail loads and, after a previous
+    // tile, the stores issued between head and tail. The counter holds at
     // most 63, so after an FP32 block the oldest 9 of its 64 stores are
     // waited for too.
     if (kEpi == kEpiBf16 && whole_prev)
@@ -910,21 +934,26 @@ void gemm_tile_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__
                         static_cast<uint16_t*>(C));
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     } else if constexpr (kOutFp32) {
-      // This epilogue does not touch LDS: the next tile's loads go first.
+      // As for BF16 C: head loads first, C parked in slot 1 four rounds of
+      // 32 rows, the tail loads after every wave has read its block back.
+      // Every wave issues exactly 64 stores (masked lanes are dropped by the
+      // store resource), so the next tile's first wait can count them.
       const Ctx cur_tile = c;
-      whole_prev = cur_tile.row0 + wy * 128 + 128 <= M && cur_tile.col0 + wx * 128 + 128 <= N;
+      whole_prev = true;
       if (pn < total) {
         set_tile<kGlu, kShufB>(c, pn, tiles_m, tiles_n);
         issue_tile_head<kFull, kGlu, kShufB>(c, tl, chunks);
       }
-      store_tile<true>(cur_tile, acc, wy, wx, r, h, C);
+      uint8_t* region = wave < 2 ? tl.a[1] + 16384 * wave : tl.b[1] + 16384 * (wave - 2);
+      store_tile_f32_lds(cur_tile, acc, wy, wx, lane, region, C);
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     } else {
       // The next tile's head loads (slot 0, chunks[0]) go out before the C
       // stores, so that they do not queue behind them; C is parked in slot 1
       // (waves 0, 1 in A's, waves 2, 3 in B's, 16 KiB each), and the tail
       // loads into slot 1 wait until every wave has read its block back.
       const Ctx cur_tile = c;
-      whole_prev = cur_tile.row0 + wy * 128 + 128 <= M && cur_tile.col0 + wx * 128 + 128 <= N;
+      whole_prev = true;  // copy_parked_rows issues 32 stores, masked lanes dropped
       if (pn < total) {
         set_tile<kGlu, kShufB>(c, pn, tiles_m, tiles_n);
         issue_tile_head<kFull, kGlu, kShufB>(c, tl, chunks);

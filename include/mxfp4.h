@@ -120,9 +120,9 @@ int mxfp4_quantize_2d_sr(const void* x_bf16, int64_t M, int64_t K, uint64_t seed
  * A_codes [M, K/2], B_codes [N, K/2]: 16-byte aligned
  * A_scales [M, K/32], B_scales [N, K/32]: 4-byte aligned
  * C [M, N] row-major BF16 or FP32: 16-byte aligned
- * M, N <= 2^31 - 1 (N <= 2^28 for BF16 C), K <= 2^24, and each buffer
- * < 2^40 bytes; otherwise MXFP4_EINVAL (or MXFP4_EALIGN for alignment) and
- * nothing is launched.
+ * M <= 2^31 - 1, N <= 2^28, K <= 2^24, and each buffer < 2^40 bytes;
+ * otherwise MXFP4_EINVAL (or MXFP4_EALIGN for alignment) and nothing is
+ * launched.
  * M <= 128 runs a split-K kernel (one 32 x 32 tile of C per workgroup, the K
  * range split between its waves and summed in LDS in a fixed order); larger
  * M runs 256 x 256 tiles. Both give the same results up to fp32 summation

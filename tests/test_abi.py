@@ -121,15 +121,16 @@ def test_gemm_rejects_oversized_buffers():
         assert mx.mxfp4_gemm_frag(P16, P16, P16, P16, big, big, 256, dt, P16, None) == EINVAL
 
 
-def test_gemm_rejects_bf16_past_2_28_columns():
-    # BF16 C: four rows of C must span at most 2^31 bytes (N <= 2^28); the
-    # buffer sizes alone (256 x (2^28 + 32) x 2 bytes < 2^40) would pass.
+@pytest.mark.parametrize("out", [mx.OUT_BF16, mx.OUT_FP32])
+def test_gemm_rejects_past_2_28_columns(out):
+    # The tile epilogue's store resource covers rows of C within 2^31 bytes
+    # (N <= 2^28); the buffer sizes alone (256 x (2^28 + 32) x 4 bytes <
+    # 2^40) would pass.
     N = (1 << 28) + 32
-    assert mx.mxfp4_gemm(P16, P16, P16, P16, 256, N, 256, mx.OUT_BF16, P16, None) == EINVAL
-    assert mx.mxfp4_gemm(P16, P16, P16, P16, 32, N, 256, mx.OUT_BF16, P16, None) == EINVAL
-    assert mx.mxfp4_gemm_bshuffled(P16, P16, P16, P16, 256, N, 256, mx.OUT_BF16, P16,
-                                   None) == EINVAL
-    assert mx.mxfp4_gemm_frag(P16, P16, P16, P16, 32, N, 256, mx.OUT_BF16, P16, None) == EINVAL
+    assert mx.mxfp4_gemm(P16, P16, P16, P16, 256, N, 256, out, P16, None) == EINVAL
+    assert mx.mxfp4_gemm(P16, P16, P16, P16, 32, N, 256, out, P16, None) == EINVAL
+    assert mx.mxfp4_gemm_bshuffled(P16, P16, P16, P16, 256, N, 256, out, P16, None) == EINVAL
+    assert mx.mxfp4_gemm_frag(P16, P16, P16, P16, 32, N, 256, out, P16, None) == EINVAL
 
 
 def test_gemm_rejects_misaligned():
