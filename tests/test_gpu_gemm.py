@@ -161,20 +161,22 @@ def _edge_transitions(M, N, workers):
 
 
 @pytest.mark.parametrize("M,N,K", [(4384, 4128, 256), (4128, 4384, 1280)])
-def test_bf16_persistent_edge_tiles(M, N, K):
-    """More tiles than workgroups with ragged M and N, BF16 out: workgroups
-    run whole tiles followed by edge tiles (and the reverse), on plain and on
-    pre-shuffled B."""
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_persistent_edge_tiles(M, N, K, out_dtype):
+    """More tiles than workgroups with ragged M and N: workgroups run whole
+    tiles followed by edge tiles (and the reverse), whose epilogues mask
+    rows and columns in their stores, on plain and on pre-shuffled B."""
     workers = torch.cuda.get_device_properties(0).multi_processor_count // 8 * 8
     wp, pw = _edge_transitions(M, N, workers)
-    announce(f"gemm bf16 {M}x{N}x{K}: {workers} workgroups, whole->edge {wp}, edge->whole {pw}")
+    announce(f"gemm {out_dtype} {M}x{N}x{K}: {workers} workgroups, whole->edge {wp}, "
+             f"edge->whole {pw}")
     assert wp > 0
     Ac, Bc = random_codes(M, K, M + 7), random_codes(N, K, N + 8)
     As, Bs = random_scales(M, K, K + 9), random_scales(N, K, K + 10)
     A, As_d, B, Bs_d = (u8_to_dev(t) for t in (Ac, As, Bc, Bs))
-    plain = mx.gemm(A, As_d, B, Bs_d, out_dtype=torch.bfloat16)
+    plain = mx.gemm(A, As_d, B, Bs_d, out_dtype=out_dtype)
     bc, bs = mx.shuffle_b(B, Bs_d)
-    shuf = mx.gemm_bshuffled(A, As_d, bc, bs, N, out_dtype=torch.bfloat16)
+    shuf = mx.gemm_bshuffled(A, As_d, bc, bs, N, out_dtype=out_dtype)
     torch.cuda.synchronize()
     c_ref, s_ref = oracle.gemm(Ac, As, Bc, Bs)
     check_gemm_output(plain, c_ref, s_ref)
@@ -209,19 +211,22 @@ def test_scale_doubling_is_exact(M):
     assert np.array_equal(np.delete(c1, 17, axis=0), np.delete(c0, 17, axis=0))
 
 
-@pytest.mark.parametrize("M", [96, 288])
-def test_output_written_exactly_in_bounds(M):
-    announce(f"gemm canary M={M}")
+@pytest.mark.parametrize("M", [96, 288, 544])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_output_written_exactly_in_bounds(M, out_dtype):
+    """C inside a larger buffer: nothing before or after it is written (the
+    tile epilogue's masked lanes are dropped by the store resource)."""
+    announce(f"gemm canary M={M} {out_dtype}")
     N, K = 320, 512
     Ac, Bc = random_codes(M, K, 51), random_codes(N, K, 52)
     As, Bs = random_scales(M, K, 53), random_scales(N, K, 54)
-    pad = 4096
-    buf = torch.full((M * N + 2 * pad,), 12345.0, dtype=torch.float32, device=DEV)
+    pad = 4 * 256 * N  # past the last row, four tiles' worth of rows
+    buf = torch.full((M * N + 2 * pad,), 12288.0, dtype=out_dtype, device=DEV)
     out = buf[pad:pad + M * N].view(M, N)
     mx.gemm(u8_to_dev(Ac), u8_to_dev(As), u8_to_dev(Bc), u8_to_dev(Bs), out=out)
     torch.cuda.synchronize()
-    b = buf.cpu().numpy()
-    assert np.all(b[:pad] == 12345.0) and np.all(b[-pad:] == 12345.0)
+    b = buf.float().cpu().numpy()
+    assert np.all(b[:pad] == 12288.0) and np.all(b[-pad:] == 12288.0)
     c_ref, s_ref = oracle.gemm(Ac, As, Bc, Bs)
     check_gemm_output(out, c_ref, s_ref)
 
