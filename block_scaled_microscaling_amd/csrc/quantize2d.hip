@@ -11,20 +11,19 @@
 // arithmetic is the one of quantize.hip (integer amax of |bits|, scale byte
 // = max(E_field(amax) - 2, 0), v_cvt_scalef32_pk_fp4_bf16 for RNE E2M1).
 //
-// Work mapping: a workgroup of 2 C threads handles one 256-row x C-column
+// Work mapping: a workgroup of 4 C threads handles one 256-row x C-column
 // tile at a time (C = 128). For round to nearest the grid is persistent
 // (two workgroups per CU) and each workgroup loads its next tile into
 // registers while it finishes the last; the stochastic variant launches one
 // workgroup per tile.
 //   Row phase: load i of thread t reads the 16-byte chunk t % (C / 8) of row
-//   16 i + t / (C / 8): C / 8 lanes per 2C-byte row segment, so each wave
+//   32 i + t / (C / 8): C / 8 lanes per 2C-byte row segment, so each wave
 //   load fetches whole lines; four consecutive lanes hold one MX block
 //   (amax finished with two quad DPP moves), and a row's codes of the tile
 //   are C / 2 bytes (half a 128-byte line). The tile is parked in LDS
 //   with rows padded by 16 bytes.
-//   Column phase: thread t takes columns 2 (t % (C / 2)), +1 and row blocks
-//   2 (t / (C / 2)), +1: 32 dword reads per row block (both columns at
-//   once), an integer amax per column, byte permutes pairing consecutive
+//   Column phase: thread t takes columns 2 (t % (C / 2)), +1 and row block
+//   t / (C / 2): 32 dword reads (both columns at once), an integer amax per column, byte permutes pairing consecutive
 //   rows, 16 conversions per column block. The column codes and scales are
 //   parked in LDS again and written with 8 lanes per 128-byte column
 //   segment: whole cache lines per store.
@@ -51,12 +50,15 @@ typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kRows = 256;
-// Tile width kC (128 or 256 columns) and its workgroup of 2 kC threads.
-template <int kC>
+// Tile width kC (128 columns) and its workgroup: kRB row blocks per thread
+// in the column phase, so 4 kC / kRB threads (256 or 512).
+template <int kC, int kRB>
 struct Geom {
-  static constexpr int kThreads = 2 * kC;
-  static constexpr int kSeg = kC / 8;         // lanes per row segment (16 bytes each)
-  static constexpr int kLdsRow = 2 * kC + 16;  // padded LDS row, bytes
+  static constexpr int kThreads = 4 * kC / kRB;
+  static constexpr int kSeg = kC / 8;              // lanes per row segment (16 bytes each)
+  static constexpr int kRowsPerLoad = kThreads / kSeg;
+  static constexpr int kLoads = kRows / kRowsPerLoad;
+  static constexpr int kLdsRow = 2 * kC + 16;      // padded LDS row, bytes
 };
 
 __device__ __forceinline__ u16x2_t abs_pair(uint32_t w) {
@@ -91,17 +93,18 @@ __device__ __forceinline__ uint32_t swap_pair(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);
 }
 
-// Loads of one tile into registers: load i covers rows 16 i + t / kSeg,
-// 16-byte chunk t % kSeg (zeros outside the matrix).
-template <int kC>
+// Loads of one tile into registers: load i covers rows kRowsPerLoad i +
+// t / kSeg, 16-byte chunk t % kSeg (zeros outside the matrix).
+template <int kC, int kRB>
 __device__ __forceinline__ void load_tile(const uint8_t* __restrict__ x, int M, int K, int m0,
-                                          int c0, int t, u32x4_t (&v)[16]) {
-  constexpr int kSeg = Geom<kC>::kSeg;
+                                          int c0, int t, u32x4_t (&v)[Geom<kC, kRB>::kLoads]) {
+  using G = Geom<kC, kRB>;
+  constexpr int kSeg = G::kSeg;
   const int64_t row_bytes = 2 * (int64_t)K;
   const int col = c0 + 8 * (t % kSeg);
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int m = m0 + 16 * i + t / kSeg;
+  for (int i = 0; i < G::kLoads; ++i) {
+    const int m = m0 + G::kRowsPerLoad * i + t / kSeg;
     v[i] = (m < M && col < K)
                ? __builtin_nontemporal_load(
                      reinterpret_cast<const u32x4_t*>(x + m * row_bytes + 2 * (int64_t)col))
@@ -142,15 +145,17 @@ __device__ __forceinline__ int visits_end(int total, int tiles_x, bool xcd_regio
 // tile_of_visit) and issues the next tile's loads as soon as the current
 // tile's rows are in LDS, so they are in flight during its column phase and
 // stores.
-template <bool kSR, int kC>
-__global__ __launch_bounds__(Geom<kC>::kThreads) void quantize_2d_kernel(
+template <bool kSR, int kC, int kRB>
+__global__ __launch_bounds__((Geom<kC, kRB>::kThreads)) void quantize_2d_kernel(
     const uint8_t* __restrict__ x, int M, int K, uint8_t* __restrict__ codes_row,
     uint8_t* __restrict__ scales_row, uint8_t* __restrict__ codes_col,
     uint8_t* __restrict__ scales_col, uint32_t key0, uint32_t key1, bool xcd_regions) {
+  using G = Geom<kC, kRB>;
   constexpr int kCols = kC;
-  constexpr int kThreads = Geom<kC>::kThreads;
-  constexpr int kSeg = Geom<kC>::kSeg;
-  constexpr int kLdsRow = Geom<kC>::kLdsRow;
+  constexpr int kThreads = G::kThreads;
+  constexpr int kSeg = G::kSeg;
+  constexpr int kLdsRow = G::kLdsRow;
+  constexpr int kRpl = G::kRowsPerLoad;
   __shared__ __align__(16) uint8_t tile[kRows * kLdsRow];
   const int t = threadIdx.x;
   const int tiles_x = (K + kCols - 1) / kCols;
@@ -165,8 +170,8 @@ __global__ __launch_bounds__(Geom<kC>::kThreads) void quantize_2d_kernel(
     p = tile_of_visit(q, total, tiles_x, xcd_regions);
   }
   if (q >= qend) return;
-  u32x4_t v[16];
-  load_tile<kC>(x, M, K, (p / tiles_x) * kRows, (p % tiles_x) * kCols, t, v);
+  u32x4_t v[G::kLoads];
+  load_tile<kC, kRB>(x, M, K, (p / tiles_x) * kRows, (p % tiles_x) * kCols, t, v);
   for (;;) {
     const int m0 = (p / tiles_x) * kRows;
     const int c0 = (p % tiles_x) * kCols;
@@ -177,8 +182,8 @@ __global__ __launch_bounds__(Geom<kC>::kThreads) void quantize_2d_kernel(
       const int odd = t & 1;
       uint32_t rnd_next[2] = {0u, 0u};  // kSR: the odd load's bytes of a pair
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int r = 16 * i + t / kSeg;
+      for (int i = 0; i < G::kLoads; ++i) {
+        const int r = kRpl * i + t / kSeg;
         *reinterpret_cast<u32x4_t*>(tile + r * kLdsRow + 16 * chunk) = v[i];
         const u32x4_t q = v[i];
         const u16x2_t mx = max2(max2(abs_pair(q[0]), abs_pair(q[1])),
@@ -190,7 +195,7 @@ __global__ __launch_bounds__(Geom<kC>::kThreads) void quantize_2d_kernel(
           // Draws for the pair of loads (i, i + 1), taken at the even one.
           uint32_t rnd[2];
           if ((i & 1) == 0) {
-            const uint32_t drow = (uint32_t)(m0 + 16 * (i + odd) + t / kSeg);
+            const uint32_t drow = (uint32_t)(m0 + kRpl * (i + odd) + t / kSeg);
             const Draw d = philox4x32_10((uint32_t)(col / 32), drow, kDirRowwise,
                                          (uint32_t)((t >> 1) & 1), key0, key1);
             const uint32_t got0 = swap_pair(odd ? d.w[0] : d.w[2]);
@@ -221,7 +226,8 @@ __global__ __launch_bounds__(Geom<kC>::kThreads) void quantize_2d_kernel(
       qn += gridDim.x;
       pn = tile_of_visit(qn, total, tiles_x, xcd_regions);
     }
-    if (qn < qend) load_tile<kC>(x, M, K, (pn / tiles_x) * kRows, (pn % tiles_x) * kCols, t, v);
+    if (qn < qend)
+      load_tile<kC, kRB>(x, M, K, (pn / tiles_x) * kRows, (pn % tiles_x) * kCols, t, v);
     __syncthreads();
 
     // Column phase: columns c0 + 2 cp, +1; row blocks 2 bp, 2 bp + 1. The
@@ -229,11 +235,11 @@ __global__ __launch_bounds__(Geom<kC>::kThreads) void quantize_2d_kernel(
     // written out with whole lines: 8 lanes per 128-byte column segment.
     const int cp = t % (kCols / 2);
     const int bp = t / (kCols / 2);
-    u32x4_t out[2][2];
-    uint32_t sbyte[2][2];
+    u32x4_t out[kRB][2];
+    uint32_t sbyte[kRB][2];
 #pragma unroll
-    for (int rbi = 0; rbi < 2; ++rbi) {
-      const int rb = 2 * bp + rbi;
+    for (int rbi = 0; rbi < kRB; ++rbi) {
+      const int rb = kRB * bp + rbi;
       uint32_t w[32];
 #pragma unroll
       for (int i = 0; i < 32; ++i)
@@ -286,8 +292,8 @@ __global__ __launch_bounds__(Geom<kC>::kThreads) void quantize_2d_kernel(
     for (int e = 0; e < 2; ++e) {
       const int c = 2 * cp + e;
 #pragma unroll
-      for (int rbi = 0; rbi < 2; ++rbi) {
-        const int rb = 2 * bp + rbi;
+      for (int rbi = 0; rbi < kRB; ++rbi) {
+        const int rb = kRB * bp + rbi;
         *reinterpret_cast<u32x4_t*>(tile + c * kColStage + 16 * rb) = out[rbi][e];
         tile[kScaleStage + 8 * c + rb] = (uint8_t)sbyte[rbi][e];
       }
@@ -295,7 +301,7 @@ __global__ __launch_bounds__(Geom<kC>::kThreads) void quantize_2d_kernel(
     __syncthreads();
     const int rows_valid = min(kRows, M - m0);  // multiple of 32
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < kCols / (kThreads / 8); ++j) {
       const int c = (kThreads / 8) * j + (t >> 3);
       const int part = t & 7;  // 16-byte part = row block
       const int k = c0 + c;
@@ -340,6 +346,12 @@ __global__ __launch_bounds__(Geom<kC>::kThreads) void quantize_2d_kernel(
 // workgroup, the loop runs once.
 constexpr int kColsRn = 128;
 constexpr int kColsSr = 128;
+// 512 threads per tile (one row block per thread in the column phase):
+// 16 waves per CU instead of 8 hide more latency (8192^2: round to nearest
+// 41.5 -> 39.4 us, stochastic 59.8 -> 55.9 us; 16384 x 14336 stochastic
+// 196 -> 179 us, round to nearest unchanged).
+constexpr int kRbRn = 1;
+constexpr int kRbSr = 1;
 constexpr int kWorkgroupsPerCu = 2;
 
 static hipError_t grid_2d(int M, int K, int cols, bool persistent, dim3& grid) {
@@ -361,7 +373,8 @@ hipError_t launch_quantize_2d(const void* x_bf16, int M, int K, void* codes_row,
   dim3 grid;
   const hipError_t e = grid_2d(M, K, kColsRn, true, grid);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((quantize_2d_kernel<false, kColsRn>), grid, dim3(Geom<kColsRn>::kThreads), 0,
+  hipLaunchKernelGGL((quantize_2d_kernel<false, kColsRn, kRbRn>), grid,
+                     dim3(Geom<kColsRn, kRbRn>::kThreads), 0,
                      stream, static_cast<const uint8_t*>(x_bf16), M, K,
                      static_cast<uint8_t*>(codes_row), static_cast<uint8_t*>(scales_row),
                      static_cast<uint8_t*>(codes_col), static_cast<uint8_t*>(scales_col), 0u, 0u,
@@ -375,7 +388,8 @@ hipError_t launch_quantize_2d_sr(const void* x_bf16, int M, int K, uint64_t seed
   dim3 grid;
   const hipError_t e = grid_2d(M, K, kColsSr, false, grid);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((quantize_2d_kernel<true, kColsSr>), grid, dim3(Geom<kColsSr>::kThreads), 0,
+  hipLaunchKernelGGL((quantize_2d_kernel<true, kColsSr, kRbSr>), grid,
+                     dim3(Geom<kColsSr, kRbSr>::kThreads), 0,
                      stream, static_cast<const uint8_t*>(x_bf16), M, K,
                      static_cast<uint8_t*>(codes_row), static_cast<uint8_t*>(scales_row),
                      static_cast<uint8_t*>(codes_col), static_cast<uint8_t*>(scales_col),
