@@ -7,13 +7,14 @@ marshals arguments. PyTorch supplies device memory and streams.
 Two layers, same names as the C ABI:
   * mxfp4_available, mxfp4_strerror, mxfp4_quantize, mxfp4_quantize_async,
     mxfp4_quantize_2d, mxfp4_quantize_sr, mxfp4_quantize_2d_sr, mxfp4_gemm,
-    mxfp4_gemm_swiglu, mxfp4_shuffle_b(_sizes), mxfp4_gemm_bshuffled,
+    mxfp4_gemm_tile, mxfp4_gemm_swiglu, mxfp4_shuffle_b(_sizes), mxfp4_gemm_bshuffled,
     mxfp4_quantize_frag, mxfp4_to_frag, mxfp4_gemm_frag take raw device
     pointers (ints) and return the C status code.
   * quantize(x), quantize_2d(x), quantize_sr(x, seed), quantize_2d_sr(x,
-    seed), gemm(...) and gemm_swiglu(...) take torch tensors, check their dtype, device,
-    shape and contiguity, allocate outputs when none are given, enqueue on
-    torch's current stream and raise Mxfp4Error on a non-zero status.
+    seed), gemm(...), gemm_tile(...) and gemm_swiglu(...) take torch tensors,
+    check their dtype, device, shape and contiguity, allocate outputs when none
+    are given, enqueue on torch's current stream and raise Mxfp4Error on a
+    non-zero status.
 
 If the library is missing the functions raise: there is no fallback path.
 """
@@ -25,7 +26,8 @@ __all__ = [
     "Mxfp4Error", "OUT_BF16", "OUT_FP32", "library_path", "load_library",
     "mxfp4_available", "mxfp4_strerror", "mxfp4_quantize", "mxfp4_quantize_async",
     "mxfp4_quantize_2d", "mxfp4_quantize_sr", "mxfp4_quantize_2d_sr", "mxfp4_gemm",
-    "mxfp4_gemm_swiglu", "quantize", "quantize_2d", "quantize_sr", "quantize_2d_sr", "gemm",
+    "mxfp4_gemm_tile", "mxfp4_gemm_swiglu", "quantize", "quantize_2d", "quantize_sr",
+    "quantize_2d_sr", "gemm", "gemm_tile",
     "gemm_swiglu", "mxfp4_shuffle_b_sizes", "mxfp4_shuffle_b", "mxfp4_gemm_bshuffled",
     "shuffle_b", "gemm_bshuffled", "mxfp4_quantize_frag", "mxfp4_to_frag", "mxfp4_gemm_frag",
     "quantize_frag", "to_frag", "gemm_frag",
@@ -71,6 +73,8 @@ def load_library():
         lib.mxfp4_quantize_2d_sr.restype = i32
         lib.mxfp4_gemm.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, vp, vp]
         lib.mxfp4_gemm.restype = i32
+        lib.mxfp4_gemm_tile.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, vp, vp]
+        lib.mxfp4_gemm_tile.restype = i32
         lib.mxfp4_gemm_swiglu.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, vp, vp, vp]
         lib.mxfp4_gemm_swiglu.restype = i32
         lib.mxfp4_shuffle_b_sizes.argtypes = [i64, i64, ctypes.POINTER(i64), ctypes.POINTER(i64)]
@@ -125,6 +129,11 @@ def mxfp4_quantize_2d_sr(x_bf16, M, K, seed, codes_row, scales_row, codes_col, s
 def mxfp4_gemm(A_codes, A_scales, B_codes, B_scales, M, N, K, out_dtype, C, stream):
     return int(load_library().mxfp4_gemm(A_codes, A_scales, B_codes, B_scales, M, N, K,
                                          out_dtype, C, stream))
+
+
+def mxfp4_gemm_tile(A_codes, A_scales, B_codes, B_scales, M, N, K, out_dtype, C, stream):
+    return int(load_library().mxfp4_gemm_tile(A_codes, A_scales, B_codes, B_scales, M, N, K,
+                                              out_dtype, C, stream))
 
 
 def mxfp4_gemm_swiglu(A_codes, A_scales, B_codes, B_scales, M, N, K, act_codes, act_scales,
@@ -289,6 +298,17 @@ def gemm(A_codes, A_scales, B_codes, B_scales, out_dtype=None, out=None, stream=
 
     out_dtype: torch.bfloat16 (default) or torch.float32.
     """
+    return _gemm_call(mxfp4_gemm, "mxfp4_gemm", A_codes, A_scales, B_codes, B_scales, out_dtype,
+                      out, stream)
+
+
+def gemm_tile(A_codes, A_scales, B_codes, B_scales, out_dtype=None, out=None, stream=None):
+    """gemm() on the 256 x 256 tile kernel whatever the shape."""
+    return _gemm_call(mxfp4_gemm_tile, "mxfp4_gemm_tile", A_codes, A_scales, B_codes, B_scales,
+                      out_dtype, out, stream)
+
+
+def _gemm_call(fn, name, A_codes, A_scales, B_codes, B_scales, out_dtype, out, stream):
     import torch
     if out_dtype is None:
         out_dtype = out.dtype if out is not None else torch.bfloat16
@@ -306,10 +326,10 @@ def gemm(A_codes, A_scales, B_codes, B_scales, out_dtype=None, out=None, stream=
         out = torch.empty((M, N), dtype=out_dtype, device=A_codes.device)
     _check(out, "out", out_dtype, (M, N))
     code = OUT_FP32 if out_dtype == torch.float32 else OUT_BF16
-    rc = mxfp4_gemm(A_codes.data_ptr(), A_scales.data_ptr(), B_codes.data_ptr(),
-                    B_scales.data_ptr(), M, N, K, code, out.data_ptr(), _stream_handle(stream))
+    rc = fn(A_codes.data_ptr(), A_scales.data_ptr(), B_codes.data_ptr(), B_scales.data_ptr(), M, N,
+            K, code, out.data_ptr(), _stream_handle(stream))
     if rc != 0:
-        raise Mxfp4Error(rc, "mxfp4_gemm")
+        raise Mxfp4Error(rc, name)
     return out
 
 

@@ -63,6 +63,40 @@ bool below_max_bytes(int64_t a, int64_t b, int64_t c = 1) {
 
 int launch_status(hipError_t e) { return e == hipSuccess ? MXFP4_OK : MXFP4_ELAUNCH; }
 
+// Argument checks shared by mxfp4_gemm and mxfp4_gemm_tile (everything but
+// the device).
+int check_gemm_args(const void* A_codes, const void* A_scales, const void* B_codes,
+                    const void* B_scales, int64_t M, int64_t N, int64_t K, int out_dtype,
+                    const void* C) {
+  if (!A_codes || !A_scales || !B_codes || !B_scales || !C) return MXFP4_EINVAL;
+  if (M <= 0 || N <= 0 || K <= 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim)
+    return MXFP4_EINVAL;
+  if (K % 256 != 0 || M % 32 != 0 || N % 32 != 0 || K > kMaxGemmK) return MXFP4_EINVAL;
+  if (out_dtype != MXFP4_OUT_BF16 && out_dtype != MXFP4_OUT_FP32) return MXFP4_EINVAL;
+  if (N > kMaxGemmN) return MXFP4_EINVAL;
+  const int64_t out_bytes = out_dtype == MXFP4_OUT_FP32 ? 4 : 2;
+  if (!below_max_bytes(M, K / 2) || !below_max_bytes(N, K / 2) ||
+      !below_max_bytes(M, N, out_bytes))
+    return MXFP4_EINVAL;
+  if (!aligned(A_codes, 16) || !aligned(B_codes, 16) || !aligned(A_scales, 4) ||
+      !aligned(B_scales, 4) || !aligned(C, 16))
+    return MXFP4_EALIGN;
+  return MXFP4_OK;
+}
+
+// mxfp4_gemm's kernel: the split-K kernel for M <= kSkinnyMaxM and for
+// problems whose 256 x 256 tiles would fill at most an eighth of the
+// persistent grid (32 tiles on 256 CUs), where one tile per CU leaves most of
+// the chip idle (measured on MI355X: 256^3 9.4 -> 2.8 us, 512 x 512 x 8192
+// 43 -> 7.3 us, 1024^2 x 8192 49 -> 25 us; at 32 tiles the two kernels take
+// about as long, at 64 the tile kernel takes half the time).
+bool gemm_uses_split_k(int64_t M, int64_t N, int workers) {
+  if (M <= mxfp4::kSkinnyMaxM) return true;
+  const int64_t tiles = ((M + mxfp4::kGemmTile - 1) / mxfp4::kGemmTile) *
+                        ((N + mxfp4::kGemmTile - 1) / mxfp4::kGemmTile);
+  return tiles * 8 <= workers;
+}
+
 }  // namespace
 
 extern "C" {
@@ -148,28 +182,31 @@ int mxfp4_quantize_2d_sr(const void* x_bf16, int64_t M, int64_t K, uint64_t seed
 int mxfp4_gemm(const void* A_codes, const void* A_scales, const void* B_codes,
                const void* B_scales, int64_t M, int64_t N, int64_t K, int out_dtype, void* C,
                void* stream) {
-  if (!A_codes || !A_scales || !B_codes || !B_scales || !C) return MXFP4_EINVAL;
-  if (M <= 0 || N <= 0 || K <= 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim)
-    return MXFP4_EINVAL;
-  if (K % 256 != 0 || M % 32 != 0 || N % 32 != 0 || K > kMaxGemmK) return MXFP4_EINVAL;
-  if (out_dtype != MXFP4_OUT_BF16 && out_dtype != MXFP4_OUT_FP32) return MXFP4_EINVAL;
-  if (N > kMaxGemmN) return MXFP4_EINVAL;
-  const int64_t out_bytes = out_dtype == MXFP4_OUT_FP32 ? 4 : 2;
-  if (!below_max_bytes(M, K / 2) || !below_max_bytes(N, K / 2) ||
-      !below_max_bytes(M, N, out_bytes))
-    return MXFP4_EINVAL;
-  if (!aligned(A_codes, 16) || !aligned(B_codes, 16) || !aligned(A_scales, 4) ||
-      !aligned(B_scales, 4) || !aligned(C, 16))
-    return MXFP4_EALIGN;
+  const int rc = check_gemm_args(A_codes, A_scales, B_codes, B_scales, M, N, K, out_dtype, C);
+  if (rc != MXFP4_OK) return rc;
   const int dev = check_device();
   if (dev != MXFP4_OK) return dev;
   const bool fp32 = out_dtype == MXFP4_OUT_FP32;
   const auto st = static_cast<hipStream_t>(stream);
-  if (M <= mxfp4::kSkinnyMaxM)
+  int workers = 0;
+  if (mxfp4::device_workers(workers) != hipSuccess) return MXFP4_ELAUNCH;
+  if (gemm_uses_split_k(M, N, workers))
     return launch_status(mxfp4::launch_gemm_skinny(A_codes, A_scales, B_codes, B_scales, (int)M,
                                                    (int)N, (int)K, fp32, C, st));
   return launch_status(mxfp4::launch_gemm(A_codes, A_scales, B_codes, B_scales, (int)M, (int)N,
                                           (int)K, fp32, C, st));
+}
+
+int mxfp4_gemm_tile(const void* A_codes, const void* A_scales, const void* B_codes,
+                    const void* B_scales, int64_t M, int64_t N, int64_t K, int out_dtype, void* C,
+                    void* stream) {
+  const int rc = check_gemm_args(A_codes, A_scales, B_codes, B_scales, M, N, K, out_dtype, C);
+  if (rc != MXFP4_OK) return rc;
+  const int dev = check_device();
+  if (dev != MXFP4_OK) return dev;
+  return launch_status(mxfp4::launch_gemm(A_codes, A_scales, B_codes, B_scales, (int)M, (int)N,
+                                          (int)K, out_dtype == MXFP4_OUT_FP32, C,
+                                          static_cast<hipStream_t>(stream)));
 }
 
 int mxfp4_shuffle_b_sizes(int64_t N, int64_t K, int64_t* code_bytes, int64_t* scale_bytes) {

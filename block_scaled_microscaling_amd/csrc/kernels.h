@@ -44,8 +44,11 @@ hipError_t launch_shuffle_b(const void* codes, const void* scales, int N, int K,
 hipError_t launch_gemm_bshuffled(const void* A, const void* As, const void* Bsh, const void* Bssh,
                                  int M, int N, int K, bool out_fp32, void* C, hipStream_t stream);
 
-// Same contract, for M up to kSkinnyMaxM: one 32 x 32 tile of C per
-// workgroup, K split between its waves.
+// Edge of the tile kernel's square tiles of C.
+constexpr int kGemmTile = 256;
+
+// Same contract, for M up to kSkinnyMaxM and for problems of few tiles: one
+// 32 x 32 tile of C per workgroup, K split between its waves.
 constexpr int kSkinnyMaxM = 128;
 hipError_t launch_gemm_skinny(const void* A, const void* As, const void* B, const void* Bs,
                               int M, int N, int K, bool out_fp32, void* C, hipStream_t stream);

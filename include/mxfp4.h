@@ -123,9 +123,11 @@ int mxfp4_quantize_2d_sr(const void* x_bf16, int64_t M, int64_t K, uint64_t seed
  * M <= 2^31 - 1, N <= 2^28, K <= 2^24, and each buffer < 2^40 bytes;
  * otherwise MXFP4_EINVAL (or MXFP4_EALIGN for alignment) and nothing is
  * launched.
- * M <= 128 runs a split-K kernel (one 32 x 32 tile of C per workgroup, the K
- * range split between its waves and summed in LDS in a fixed order); larger
- * M runs 256 x 256 tiles. Both give the same results up to fp32 summation
+ * M <= 128, and problems of at most CUs / 8 tiles of 256 x 256 (32 tiles
+ * on a 256-CU MI355X), run a split-K kernel (one 32 x 32 tile of C per
+ * workgroup, the K range split between its waves and summed in LDS in a
+ * fixed order); larger problems run 256 x 256 tiles on a persistent grid of
+ * one workgroup per CU. Both give the same results up to fp32 summation
  * order.
  * Accuracy: each 64-wide K slice is one block-scaled MFMA whose sum is added
  * to an fp32 accumulator with one rounding, so the 256 x 256 kernel takes
@@ -139,6 +141,16 @@ int mxfp4_quantize_2d_sr(const void* x_bf16, int64_t M, int64_t K, uint64_t seed
 int mxfp4_gemm(const void* A_codes, const void* A_scales, const void* B_codes,
                const void* B_scales, int64_t M, int64_t N, int64_t K, int out_dtype,
                void* C, void* stream);
+
+/* mxfp4_gemm on the 256 x 256 tile kernel whatever the shape: the same
+ * operation (the a4w4 GEMM of "Initial integration of a4w4 GEMM",
+ * ROCm/TransformerEngine #663, under the gates above), for callers that
+ * choose the kernel themselves, e.g. to keep one summation order across
+ * shapes. Arguments, layouts, requirements, accuracy bound and errors as
+ * mxfp4_gemm; asynchronous on `stream`. */
+int mxfp4_gemm_tile(const void* A_codes, const void* A_scales, const void* B_codes,
+                    const void* B_scales, int64_t M, int64_t N, int64_t K, int out_dtype,
+                    void* C, void* stream);
 
 /* Pre-shuffled weights. The a4w4 path of "Integrate MXFP4 hipblaslt GEMM
  * support" (#697, Changes list) and the call reviewed on "Initial integration

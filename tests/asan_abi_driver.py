@@ -29,6 +29,7 @@ def main(path):
         "mxfp4_quantize_sr": ([vp, i64, i64, u64, vp, vp, vp], i32),
         "mxfp4_quantize_2d_sr": ([vp, i64, i64, u64, vp, vp, vp, vp, vp], i32),
         "mxfp4_gemm": ([vp, vp, vp, vp, i64, i64, i64, i32, vp, vp], i32),
+        "mxfp4_gemm_tile": ([vp, vp, vp, vp, i64, i64, i64, i32, vp, vp], i32),
         "mxfp4_gemm_swiglu": ([vp, vp, vp, vp, i64, i64, i64, vp, vp, vp, vp], i32),
         "mxfp4_shuffle_b_sizes": ([i64, i64, ctypes.POINTER(i64), ctypes.POINTER(i64)], i32),
         "mxfp4_shuffle_b": ([vp, vp, i64, i64, vp, vp, vp], i32),
@@ -59,12 +60,15 @@ def main(path):
     for M, N, K in [(0, 32, 256), (32, 0, 256), (32, 32, 0), (31, 32, 256), (32, 33, 256),
                     (32, 32, 255), (32, 32, 1 << 25), (1 << 31, 32, 256)]:
         expect(L.mxfp4_gemm(P, P, P, P, M, N, K, 0, P, None), EINVAL, f"gemm {M}x{N}x{K}")
+        expect(L.mxfp4_gemm_tile(P, P, P, P, M, N, K, 0, P, None), EINVAL, "gemm_tile")
         expect(L.mxfp4_gemm_bshuffled(P, P, P, P, M, N, K, 0, P, None), EINVAL, "bshuffled")
         expect(L.mxfp4_gemm_frag(P, P, P, P, M, N, K, 0, P, None), EINVAL, "frag")
     # M * N * 4 past int64 (M = N = 2^31 - 32, FP32): rejected, never wrapped.
     big = (1 << 31) - 32
     for dt in (0, 1):
         expect(L.mxfp4_gemm(P, P, P, P, big, big, 256, dt, P, None), EINVAL, "gemm M*N huge")
+        expect(L.mxfp4_gemm_tile(P, P, P, P, big, big, 256, dt, P, None), EINVAL,
+               "gemm_tile M*N huge")
         expect(L.mxfp4_gemm_bshuffled(P, P, P, P, big, big, 256, dt, P, None), EINVAL,
                "bshuffled M*N huge")
         expect(L.mxfp4_gemm_frag(P, P, P, P, big, big, 256, dt, P, None), EINVAL,
@@ -76,6 +80,7 @@ def main(path):
     expect(L.mxfp4_gemm(P + 8, P, P, P, 32, 32, 256, 0, P, None), EALIGN, "gemm align")
     expect(L.mxfp4_gemm(P, P + 2, P, P, 32, 32, 256, 0, P, None), EALIGN, "gemm scale align")
     expect(L.mxfp4_gemm(P, P, P, P, 32, 32, 256, 0, P + 8, None), EALIGN, "gemm C align")
+    expect(L.mxfp4_gemm_tile(P + 8, P, P, P, 32, 32, 256, 0, P, None), EALIGN, "tile align")
     for M, K in [(0, 32), (4, 0), (4, 33), (1 << 31, 32), (1 << 21, 1 << 20)]:
         expect(L.mxfp4_quantize(P, M, K, P, P), EINVAL, f"quantize {M}x{K}")
         expect(L.mxfp4_quantize_async(P, M, K, P, P, None), EINVAL, "quantize_async")
@@ -109,7 +114,8 @@ def main(path):
     if present == 0:
         U = EUNSUPPORTED
         expect(L.mxfp4_gemm(P, P, P, P, 32, 32, 256, 0, P, None), U, "gemm")
-        expect(L.mxfp4_gemm(P, P, P, P, 256, 256, 1024, 1, P, None), U, "gemm tile")
+        expect(L.mxfp4_gemm(P, P, P, P, 256, 256, 1024, 1, P, None), U, "gemm 256^2")
+        expect(L.mxfp4_gemm_tile(P, P, P, P, 256, 256, 1024, 1, P, None), U, "gemm_tile")
         expect(L.mxfp4_quantize(P, 4, 32, P, P), U, "quantize")
         expect(L.mxfp4_quantize_2d(P, 32, 32, P, P, P, P, None), U, "2d")
         expect(L.mxfp4_quantize_sr(P, 4, 32, 5, P, P, None), U, "sr")

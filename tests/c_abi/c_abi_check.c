@@ -133,6 +133,17 @@ int main(void) {
     for (int n = 0; n < N; ++n) bad32 += (double)h32[m * N + n] != expected(m, n);
   check(bad32 == 0, "fragment-order FP32 GEMM equals its closed form");
 
+  /* The tile kernel named explicitly: same closed form. */
+  HIP_OK(hipMemset(c32, 0, sizeof(float) * M * N));
+  check(mxfp4_gemm_tile(ac, as, bc, bs, M, N, K, MXFP4_OUT_FP32, c32, NULL) == MXFP4_OK,
+        "mxfp4_gemm_tile");
+  HIP_OK(hipDeviceSynchronize());
+  HIP_OK(hipMemcpy(h32, c32, sizeof(float) * M * N, hipMemcpyDeviceToHost));
+  bad32 = 0;
+  for (int m = 0; m < M; ++m)
+    for (int n = 0; n < N; ++n) bad32 += (double)h32[m * N + n] != expected(m, n);
+  check(bad32 == 0, "tile-kernel FP32 GEMM equals its closed form");
+
   /* Rejected calls return their status and launch nothing. */
   check(mxfp4_gemm(ac, as, bc, bs, M, N, 100, MXFP4_OUT_FP32, c32, NULL) == MXFP4_EINVAL,
         "K % 256 != 0 is rejected");

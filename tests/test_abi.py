@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
     lib = mx.load_library()
     names = _declared_functions()
     assert names == ["mxfp4_available", "mxfp4_gemm", "mxfp4_gemm_bshuffled",
-                     "mxfp4_gemm_frag", "mxfp4_gemm_swiglu", "mxfp4_quantize",
+                     "mxfp4_gemm_frag", "mxfp4_gemm_swiglu", "mxfp4_gemm_tile", "mxfp4_quantize",
                      "mxfp4_quantize_2d", "mxfp4_quantize_2d_sr", "mxfp4_quantize_async",
                      "mxfp4_quantize_frag", "mxfp4_quantize_sr", "mxfp4_shuffle_b",
                      "mxfp4_shuffle_b_sizes", "mxfp4_strerror", "mxfp4_to_frag"]
@@ -52,17 +52,19 @@ def test_strerror_texts():
     (1 << 31, 32, 256), (32, 32, (1 << 31) + 256), (32, 32, (1 << 24) + 256),
 ])
 def test_gemm_rejects_bad_sizes(M, N, K):
-    assert mx.mxfp4_gemm(P16, P16, P16, P16, M, N, K, mx.OUT_BF16, P16, None) == EINVAL
+    for fn in (mx.mxfp4_gemm, mx.mxfp4_gemm_tile):
+        assert fn(P16, P16, P16, P16, M, N, K, mx.OUT_BF16, P16, None) == EINVAL
 
 
 def test_gemm_rejects_bad_dtype_and_nulls():
-    assert mx.mxfp4_gemm(P16, P16, P16, P16, 32, 32, 256, 2, P16, None) == EINVAL
-    assert mx.mxfp4_gemm(P16, P16, P16, P16, 32, 32, 256, -1, P16, None) == EINVAL
-    for i in range(5):
-        ptrs = [P16] * 5
-        ptrs[i] = None
-        a, as_, b, bs, c = ptrs
-        assert mx.mxfp4_gemm(a, as_, b, bs, 32, 32, 256, mx.OUT_FP32, c, None) == EINVAL
+    for fn in (mx.mxfp4_gemm, mx.mxfp4_gemm_tile):
+        assert fn(P16, P16, P16, P16, 32, 32, 256, 2, P16, None) == EINVAL
+        assert fn(P16, P16, P16, P16, 32, 32, 256, -1, P16, None) == EINVAL
+        for i in range(5):
+            ptrs = [P16] * 5
+            ptrs[i] = None
+            a, as_, b, bs, c = ptrs
+            assert fn(a, as_, b, bs, 32, 32, 256, mx.OUT_FP32, c, None) == EINVAL
 
 
 @pytest.mark.parametrize("M,N,K", [
@@ -116,6 +118,7 @@ def test_gemm_rejects_oversized_buffers():
     big = (1 << 31) - 32
     for dt in (mx.OUT_BF16, mx.OUT_FP32):
         assert mx.mxfp4_gemm(P16, P16, P16, P16, big, big, 256, dt, P16, None) == EINVAL
+        assert mx.mxfp4_gemm_tile(P16, P16, P16, P16, big, big, 256, dt, P16, None) == EINVAL
         assert mx.mxfp4_gemm_bshuffled(P16, P16, P16, P16, big, big, 256, dt, P16,
                                        None) == EINVAL
         assert mx.mxfp4_gemm_frag(P16, P16, P16, P16, big, big, 256, dt, P16, None) == EINVAL
@@ -129,6 +132,7 @@ def test_gemm_rejects_past_2_28_columns(out):
     N = (1 << 28) + 32
     assert mx.mxfp4_gemm(P16, P16, P16, P16, 256, N, 256, out, P16, None) == EINVAL
     assert mx.mxfp4_gemm(P16, P16, P16, P16, 32, N, 256, out, P16, None) == EINVAL
+    assert mx.mxfp4_gemm_tile(P16, P16, P16, P16, 256, N, 256, out, P16, None) == EINVAL
     assert mx.mxfp4_gemm_bshuffled(P16, P16, P16, P16, 256, N, 256, out, P16, None) == EINVAL
     assert mx.mxfp4_gemm_frag(P16, P16, P16, P16, 32, N, 256, out, P16, None) == EINVAL
 
@@ -139,9 +143,9 @@ def test_gemm_rejects_misaligned():
                      ("Bs", P16 + 1)]:
         a = dict(args)
         a[key] = bad
-        rc = mx.mxfp4_gemm(a["A"], a["As"], a["B"], a["Bs"], 32, 32, 256, mx.OUT_BF16,
-                           a["C"], None)
-        assert rc == EALIGN, key
+        for fn in (mx.mxfp4_gemm, mx.mxfp4_gemm_tile):
+            rc = fn(a["A"], a["As"], a["B"], a["Bs"], 32, 32, 256, mx.OUT_BF16, a["C"], None)
+            assert rc == EALIGN, key
 
 
 @pytest.mark.parametrize("M,K", [(0, 32), (-1, 32), (4, 0), (4, 16), (4, 48), (4, 33),
@@ -198,6 +202,8 @@ def test_no_device_reports_unsupported():
     if mx.mxfp4_available() != 0:
         pytest.skip("a gfx950 device is present; stand-in pointers must not reach it")
     assert mx.mxfp4_gemm(P16, P16, P16, P16, 32, 32, 256, mx.OUT_BF16, P16, None) == EUNSUPPORTED
+    assert mx.mxfp4_gemm_tile(P16, P16, P16, P16, 32, 32, 256, mx.OUT_BF16, P16,
+                              None) == EUNSUPPORTED
     assert mx.mxfp4_quantize(P16, 4, 32, P16, P16) == EUNSUPPORTED
     assert mx.mxfp4_quantize_2d(P16, 32, 32, P16, P16, P16, P16, None) == EUNSUPPORTED
     assert mx.mxfp4_quantize_sr(P16, 4, 32, 5, P16, P16, None) == EUNSUPPORTED

@@ -9,9 +9,12 @@ documented in oracle/compare.py). The non-zero count check guards against the
 silent all-zeros failure reported on "feat(ck-tile): aquant GEMM TE to
 dispatcher bridge" (rocm-libraries #9980, GPU validation).
 
-The library runs M <= 128 on the split-K kernel and larger M on the 256 x 256
-tile kernel, so each layout case runs at M = 32 (or the case's own small M)
-and again with its rows repeated past 128.
+mxfp4_gemm runs M <= 128, and problems of at most CUs / 8 tiles of 256 x 256,
+on the split-K kernel and larger problems on the 256 x 256 tile kernel;
+mxfp4_gemm_tile runs the tile kernel whatever the shape. Each layout case runs
+at M = 32 (or the case's own small M), and again with its rows repeated past
+128 through mxfp4_gemm (split-K kernel, several row tiles) and through
+mxfp4_gemm_tile.
 """
 
 import numpy as np
@@ -35,9 +38,10 @@ def _assert_not_silent_zeros(got, c_ref, s_ref):
     assert np.count_nonzero(got[significant]) == int(significant.sum())
 
 
-# Row counts that reach each kernel: 32 -> split-K kernel (M <= 128),
-# 160 -> tile kernel.
-KERNEL_ROWS = [32, 160]
+# (rows, entry point): the split-K kernel at one and at five row tiles
+# (mxfp4_gemm), the tile kernel (mxfp4_gemm_tile).
+KERNEL_CASES = [(32, "auto"), (160, "auto"), (160, "tile")]
+ENTRY = {"auto": mx.gemm, "tile": mx.gemm_tile}
 
 
 def _rep(x, rows):
@@ -45,29 +49,30 @@ def _rep(x, rows):
     return np.tile(x, (rows // x.shape[0],) + (1,) * (x.ndim - 1))
 
 
-def _gemm(Ac, As, Bc, Bs, out_dtype):
-    out = mx.gemm(u8_to_dev(Ac), u8_to_dev(As), u8_to_dev(Bc), u8_to_dev(Bs), out_dtype=out_dtype)
+def _gemm(Ac, As, Bc, Bs, out_dtype, kernel="auto"):
+    out = ENTRY[kernel](u8_to_dev(Ac), u8_to_dev(As), u8_to_dev(Bc), u8_to_dev(Bs),
+                        out_dtype=out_dtype)
     torch.cuda.synchronize()
     return out
 
 
-@pytest.mark.parametrize("rows", KERNEL_ROWS)
+@pytest.mark.parametrize("rows,kernel", KERNEL_CASES)
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
-def test_single_tile_random(out_dtype, rows):
+def test_single_tile_random(out_dtype, rows, kernel):
     """One 32 x 32 x 256 problem: pins the MFMA operand/scale lane layout."""
-    announce(f"gemm {rows}x32x256 random {out_dtype}")
+    announce(f"gemm {rows}x32x256 random {out_dtype} ({kernel})")
     Ac, Bc = random_codes(rows, 256, 1), random_codes(32, 256, 2)
     As, Bs = random_scales(rows, 256, 3), random_scales(32, 256, 4)
-    out = _gemm(Ac, As, Bc, Bs, out_dtype)
+    out = _gemm(Ac, As, Bc, Bs, out_dtype, kernel)
     c_ref, s_ref = oracle.gemm(Ac, As, Bc, Bs)
     check_gemm_output(out, c_ref, s_ref)
 
 
-@pytest.mark.parametrize("rows", KERNEL_ROWS)
-def test_hand_worked_g1_padded(rows):
+@pytest.mark.parametrize("rows,kernel", KERNEL_CASES)
+def test_hand_worked_g1_padded(rows, kernel):
     """Q1 block x unit B rows (1 x 32 x 32 by hand), padded to rows x 32 x 256
     with zero codes: row 0 of C is the dequantized Q1 block."""
-    announce(f"gemm G1 padded to {rows} rows")
+    announce(f"gemm G1 padded to {rows} rows ({kernel})")
     g = read_golden("q1_block.txt")
     Ac = np.zeros((rows, 128), np.uint8)
     Ac[0, :16] = [int(v, 16) for v in g["packed"]]
@@ -75,14 +80,14 @@ def test_hand_worked_g1_padded(rows):
     Bc = np.zeros((32, 128), np.uint8)
     for n in range(32):
         Bc[n, n // 2] = 2 << (4 * (n % 2))
-    out = _gemm(Ac, As, Bc, As[:32], torch.float32).cpu().numpy()
+    out = _gemm(Ac, As, Bc, As[:32], torch.float32, kernel).cpu().numpy()
     assert out[0].tolist() == [float(v) for v in g["dequant"]]
     assert np.all(out[1:] == 0)
 
 
-@pytest.mark.parametrize("rows", KERNEL_ROWS)
-def test_hand_worked_g2_g3_g4(rows):
-    announce(f"gemm G2 G3 G4 at {rows} rows")
+@pytest.mark.parametrize("rows,kernel", KERNEL_CASES)
+def test_hand_worked_g2_g3_g4(rows, kernel):
+    announce(f"gemm G2 G3 G4 at {rows} rows ({kernel})")
     n = np.arange(32)
     m = np.arange(32)[:, None]
     # G2: C = 255 * 2^(n % 3)
@@ -90,12 +95,12 @@ def test_hand_worked_g2_g3_g4(rows):
     As = np.tile(np.arange(123, 131, dtype=np.uint8), (32, 1))
     Bs = (126 + n % 3).astype(np.uint8)[:, None].repeat(8, axis=1)
     for dt in (torch.float32, torch.bfloat16):
-        out = _gemm(_rep(A, rows), _rep(As, rows), A, Bs, dt).float().cpu().numpy()
+        out = _gemm(_rep(A, rows), _rep(As, rows), A, Bs, dt, kernel).float().cpu().numpy()
         assert np.array_equal(out, np.tile(255.0 * 2.0 ** (n % 3), (rows, 1)))
     # G3: nibble pairing, C = 448 everywhere
     s = np.full((32, 8), 127, np.uint8)
     out = _gemm(_rep(np.full((32, 128), 0x13, np.uint8), rows), _rep(s, rows),
-                np.full((32, 128), 0x24, np.uint8), s, torch.float32).cpu().numpy()
+                np.full((32, 128), 0x24, np.uint8), s, torch.float32, kernel).cpu().numpy()
     assert out.shape == (rows, 32) and np.all(out == 448.0)
     # G4: scale-to-block mapping, C = 2338 * 2^(m%2 + n%4 - 2)
     A = np.zeros((32, 128), np.uint8)
@@ -104,7 +109,7 @@ def test_hand_worked_g2_g3_g4(rows):
     As = (123 + np.arange(8)[None, :] + (np.arange(32) % 2)[:, None]).astype(np.uint8)
     B = np.full((32, 128), 0x22, np.uint8)
     Bs = (125 + n % 4).astype(np.uint8)[:, None].repeat(8, axis=1)
-    out = _gemm(_rep(A, rows), _rep(As, rows), B, Bs, torch.float32).cpu().numpy()
+    out = _gemm(_rep(A, rows), _rep(As, rows), B, Bs, torch.float32, kernel).cpu().numpy()
     assert np.array_equal(out, _rep(2338.0 * 2.0 ** ((m % 2) + (n[None, :] % 4) - 2), rows))
 
 
@@ -116,13 +121,15 @@ def test_hand_worked_g2_g3_g4(rows):
                                    (96, 320, 2304), (128, 64, 256), (128, 288, 768),
                                    (32, 96, 14336), (64, 2080, 7936)])
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
-def test_random_operands_many_tiles(M, N, K, out_dtype):
+@pytest.mark.parametrize("kernel", ["auto", "tile"])
+def test_random_operands_many_tiles(M, N, K, out_dtype, kernel):
     """Uniform random code bytes (every code, both signs) and scales 117..137,
-    shapes spanning several 256-tiles with ragged M and N edges."""
-    announce(f"gemm random {M}x{N}x{K} {out_dtype}")
+    shapes spanning several 256-tiles with ragged M and N edges, through
+    mxfp4_gemm (the split-K kernel at these sizes) and the tile kernel."""
+    announce(f"gemm random {M}x{N}x{K} {out_dtype} ({kernel})")
     Ac, Bc = random_codes(M, K, M + 1), random_codes(N, K, N + 2)
     As, Bs = random_scales(M, K, K + 3), random_scales(N, K, K + 4)
-    out = _gemm(Ac, As, Bc, Bs, out_dtype)
+    out = _gemm(Ac, As, Bc, Bs, out_dtype, kernel)
     c_ref, s_ref = oracle.gemm(Ac, As, Bc, Bs)
     check_gemm_output(out, c_ref, s_ref)
     _assert_not_silent_zeros(out.float().cpu().numpy(), c_ref, s_ref)
@@ -175,55 +182,58 @@ def test_persistent_edge_tiles(M, N, K, out_dtype):
     As, Bs = random_scales(M, K, K + 9), random_scales(N, K, K + 10)
     A, As_d, B, Bs_d = (u8_to_dev(t) for t in (Ac, As, Bc, Bs))
     plain = mx.gemm(A, As_d, B, Bs_d, out_dtype=out_dtype)
+    tile = mx.gemm_tile(A, As_d, B, Bs_d, out_dtype=out_dtype)
     bc, bs = mx.shuffle_b(B, Bs_d)
     shuf = mx.gemm_bshuffled(A, As_d, bc, bs, N, out_dtype=out_dtype)
     torch.cuda.synchronize()
     c_ref, s_ref = oracle.gemm(Ac, As, Bc, Bs)
     check_gemm_output(plain, c_ref, s_ref)
+    assert torch.equal(plain, tile), "mxfp4_gemm did not run the tile kernel at this size"
     assert torch.equal(plain, shuf)
 
 
-@pytest.mark.parametrize("M", [96, 288])
-def test_wide_scale_range(M):
+@pytest.mark.parametrize("M,kernel", [(96, "auto"), (288, "auto"), (288, "tile")])
+def test_wide_scale_range(M, kernel):
     """Scales 100..150 on both sides: products span 2^-54 .. 2^46."""
-    announce(f"gemm wide scale range M={M}")
+    announce(f"gemm wide scale range M={M} ({kernel})")
     N, K = 160, 1280
     Ac, Bc = random_codes(M, K, 31), random_codes(N, K, 32)
     As, Bs = random_scales(M, K, 33, 100, 150), random_scales(N, K, 34, 100, 150)
-    out = _gemm(Ac, As, Bc, Bs, torch.float32)
+    out = _gemm(Ac, As, Bc, Bs, torch.float32, kernel)
     c_ref, s_ref = oracle.gemm(Ac, As, Bc, Bs)
     check_gemm_output(out, c_ref, s_ref)
 
 
-@pytest.mark.parametrize("M", [64, 288])
-def test_scale_doubling_is_exact(M):
+@pytest.mark.parametrize("M,kernel", [(64, "auto"), (288, "auto"), (288, "tile")])
+def test_scale_doubling_is_exact(M, kernel):
     """Adding 1 to every A scale of one row doubles that C row bit for bit
     (power-of-two scaling commutes with fp32 rounding) and leaves the others."""
-    announce(f"gemm scale doubling invariant M={M}")
+    announce(f"gemm scale doubling invariant M={M} ({kernel})")
     N, K = 288, 1024
     Ac, Bc = random_codes(M, K, 41), random_codes(N, K, 42)
     As, Bs = random_scales(M, K, 43), random_scales(N, K, 44)
-    c0 = _gemm(Ac, As, Bc, Bs, torch.float32).cpu().numpy()
+    c0 = _gemm(Ac, As, Bc, Bs, torch.float32, kernel).cpu().numpy()
     As2 = As.copy()
     As2[17] += 1
-    c1 = _gemm(Ac, As2, Bc, Bs, torch.float32).cpu().numpy()
+    c1 = _gemm(Ac, As2, Bc, Bs, torch.float32, kernel).cpu().numpy()
     assert np.array_equal(c1[17], 2 * c0[17])
     assert np.array_equal(np.delete(c1, 17, axis=0), np.delete(c0, 17, axis=0))
 
 
-@pytest.mark.parametrize("M", [96, 288, 544])
+@pytest.mark.parametrize("M,kernel", [(96, "auto"), (288, "auto"), (288, "tile"),
+                                      (544, "tile")])
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
-def test_output_written_exactly_in_bounds(M, out_dtype):
+def test_output_written_exactly_in_bounds(M, kernel, out_dtype):
     """C inside a larger buffer: nothing before or after it is written (the
     tile epilogue's masked lanes are dropped by the store resource)."""
-    announce(f"gemm canary M={M} {out_dtype}")
+    announce(f"gemm canary M={M} {out_dtype} ({kernel})")
     N, K = 320, 512
     Ac, Bc = random_codes(M, K, 51), random_codes(N, K, 52)
     As, Bs = random_scales(M, K, 53), random_scales(N, K, 54)
     pad = 4 * 256 * N  # past the last row, four tiles' worth of rows
     buf = torch.full((M * N + 2 * pad,), 12288.0, dtype=out_dtype, device=DEV)
     out = buf[pad:pad + M * N].view(M, N)
-    mx.gemm(u8_to_dev(Ac), u8_to_dev(As), u8_to_dev(Bc), u8_to_dev(Bs), out=out)
+    ENTRY[kernel](u8_to_dev(Ac), u8_to_dev(As), u8_to_dev(Bc), u8_to_dev(Bs), out=out)
     torch.cuda.synchronize()
     b = buf.float().cpu().numpy()
     assert np.all(b[:pad] == 12288.0) and np.all(b[-pad:] == 12288.0)
@@ -326,8 +336,9 @@ def test_workload_mlp_whole_rows(name):
 
 @pytest.mark.parametrize("M", [32, 256])
 def test_maximum_k_closed_form(M):
-    """K = 2^24, the largest K the GEMM accepts, on both kernels, on the
-    pre-shuffled path and (M = 32) on the fragment-order path. A is all 1.0 (scale 127); row n of B holds 1.0 at
+    """K = 2^24, the largest K the GEMM accepts, on both kernels (mxfp4_gemm
+    runs the split-K kernel at both M, mxfp4_gemm_tile the tile kernel), on
+    the pre-shuffled path and (M = 32) on the fragment-order path. A is all 1.0 (scale 127); row n of B holds 1.0 at
     every k with k % 8192 == 2 n (2048 of them) under scale 127 + n % 3, so
     C[m, n] = 2048 * 2^(n % 3) exactly: every K block of the range counts,
     and any offset overflow along K would change the sums."""
@@ -342,9 +353,11 @@ def test_maximum_k_closed_form(M):
     b_scales = (127 + (n % 3)).to(torch.uint8)[:, None].expand(N, K // 32).contiguous()
     want = (2048.0 * 2.0 ** (n % 3).float())[None, :].expand(M, N)
     for dt in (torch.float32, torch.bfloat16):
-        got = mx.gemm(a_codes, a_scales, b_codes, b_scales, out_dtype=dt)
-        torch.cuda.synchronize()
-        assert torch.equal(got.float(), want), dt
+        for entry in (mx.gemm, mx.gemm_tile):
+            got = entry(a_codes, a_scales, b_codes, b_scales, out_dtype=dt)
+            torch.cuda.synchronize()
+            assert torch.equal(got.float(), want), (dt, entry.__name__)
+            del got
     bc, bs = mx.shuffle_b(b_codes, b_scales)
     got = mx.gemm_bshuffled(a_codes, a_scales, bc, bs, N, out_dtype=torch.float32)
     torch.cuda.synchronize()
@@ -364,15 +377,17 @@ def test_fp32_accumulation_worst_case(M, K):
     """A large partial sum first and half-ulp slices after it: every
     sequential fp32 rounding loses its slice. The closed form of C is
     8192 + (K - 256) 2^-17 (all products positive, so S = C); the error must
-    stay within fp32_rel_tol(K) * S on the split-K (M = 32), tile (M = 256)
-    and fragment-order kernels, and within 1e-5 * S up to K = 8192."""
+    stay within fp32_rel_tol(K) * S on the split-K (mxfp4_gemm at both M),
+    tile (mxfp4_gemm_tile) and fragment-order kernels, and within 1e-5 * S up
+    to K = 8192."""
     N = 64
     announce(f"fp32 accumulation worst case M={M} K={K}")
     ac, as_ = large_block_first(M, K, 127)
     bc, bs = large_block_first(N, K, 128)
     exact = 8192.0 + (K - 256) * 2.0 ** -17
     A, As_, B, Bs = (u8_to_dev(t) for t in (ac, as_, bc, bs))
-    outs = {"gemm": mx.gemm(A, As_, B, Bs, out_dtype=torch.float32)}
+    outs = {"gemm": mx.gemm(A, As_, B, Bs, out_dtype=torch.float32),
+            "gemm_tile": mx.gemm_tile(A, As_, B, Bs, out_dtype=torch.float32)}
     if M <= 128:
         af, asf = mx.to_frag(A, As_)
         bf, bsf = mx.to_frag(B, Bs)
@@ -389,15 +404,15 @@ def test_fp32_accumulation_worst_case(M, K):
 
 
 @pytest.mark.parametrize("K", [65536, 262144])
-@pytest.mark.parametrize("M", [32, 160])
-def test_fp32_random_operands_long_k(M, K):
+@pytest.mark.parametrize("M,kernel", [(32, "auto"), (160, "tile")])
+def test_fp32_random_operands_long_k(M, kernel, K):
     """Random codes and scales at K far past the workloads' 14336, on both
     kernels, against the oracle at fp32_rel_tol(K)."""
     N = 64
-    announce(f"gemm random fp32 {M}x{N}x{K}")
+    announce(f"gemm random fp32 {M}x{N}x{K} ({kernel})")
     Ac, Bc = random_codes(M, K, K + M), random_codes(N, K, K + 1)
     As, Bs = random_scales(M, K, K + 2), random_scales(N, K, K + 3)
-    out = _gemm(Ac, As, Bc, Bs, torch.float32)
+    out = _gemm(Ac, As, Bc, Bs, torch.float32, kernel)
     c_ref, s_ref = oracle.gemm(Ac, As, Bc, Bs)
     check_gemm_output(out, c_ref, s_ref, K=K)
     _assert_not_silent_zeros(out.cpu().numpy(), c_ref, s_ref)

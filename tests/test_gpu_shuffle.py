@@ -75,14 +75,14 @@ def test_shuffled_gemm_matches_oracle(M, N, K, out):
 
 @pytest.mark.parametrize("M,N,K", [(512, 768, 2048), (288, 544, 1280)])
 def test_shuffled_gemm_equals_plain_gemm(M, N, K):
-    """Same tile kernel, same MFMA order: identical bits."""
-    announce(f"gemm_bshuffled == gemm {M}x{N}x{K}")
+    """Same tile kernel (mxfp4_gemm_tile), same MFMA order: identical bits."""
+    announce(f"gemm_bshuffled == gemm_tile {M}x{N}x{K}")
     a_c, a_s = _random_operand(M, K, 11)
     b_c, b_s = _random_operand(N, K, 12)
     A, As_, B, Bs = (u8_to_dev(t) for t in (a_c, a_s, b_c, b_s))
     bc, bs = mx.shuffle_b(B, Bs)
     for dt in (torch.float32, torch.bfloat16):
-        plain = mx.gemm(A, As_, B, Bs, out_dtype=dt)
+        plain = mx.gemm_tile(A, As_, B, Bs, out_dtype=dt)
         shuf = mx.gemm_bshuffled(A, As_, bc, bs, N, out_dtype=dt)
         torch.cuda.synchronize()
         assert torch.equal(plain, shuf)
