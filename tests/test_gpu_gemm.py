@@ -135,6 +135,29 @@ def test_random_operands_many_tiles(M, N, K, out_dtype, kernel):
     _assert_not_silent_zeros(out.float().cpu().numpy(), c_ref, s_ref)
 
 
+@pytest.mark.parametrize("N", [2048, 2080])
+def test_kernel_choice_boundary(N):
+    """1024 x N: 4 x 8 = 32 tiles of 256 x 256 (CUs / 8 on a 256-CU part:
+    mxfp4_gemm runs the split-K kernel) and 4 x 9 = 36 tiles (the tile kernel,
+    so its bits equal mxfp4_gemm_tile's). Both against the oracle."""
+    M, K = 1024, 512
+    workers = torch.cuda.get_device_properties(0).multi_processor_count // 8 * 8
+    tiles = (M // 256) * (-(-N // 256))
+    announce(f"gemm kernel choice {M}x{N}x{K}: {tiles} tiles, {workers} workgroups")
+    Ac, Bc = random_codes(M, K, 71), random_codes(N, K, 72)
+    As, Bs = random_scales(M, K, 73), random_scales(N, K, 74)
+    args = [u8_to_dev(t) for t in (Ac, As, Bc, Bs)]
+    c_ref, s_ref = oracle.gemm(Ac, As, Bc, Bs)
+    for dt in (torch.bfloat16, torch.float32):
+        auto = mx.gemm(*args, out_dtype=dt)
+        tile = mx.gemm_tile(*args, out_dtype=dt)
+        torch.cuda.synchronize()
+        if tiles * 8 > workers:
+            assert torch.equal(auto, tile)
+        check_gemm_output(auto, c_ref, s_ref)
+        check_gemm_output(tile, c_ref, s_ref)
+
+
 def _tile_of(pid, tiles_m, tiles_n, n_xcd=8, group_m=4):
     """The tile kernel's XCD-aware tile order (tile id -> tile row, column)."""
     total = tiles_m * tiles_n
