@@ -277,8 +277,9 @@ def to_dev(torch, bits, dev):
 
 def bench_config(torch, mx, dev, stream, time_kernel, w, oracle_sample=True, traffic=None):
     """GEMM and activation-quantize times of workload `w` (contract entries,
-    and the faster layout variant: pre-shuffled B for M > 128, fragment order
-    for M <= 128), with operand copies rotated past the LLC."""
+    and a layout variant: fragment order for GEMMs shorter than a host launch
+    (M <= 128 or under 0.1 TFLOP), pre-shuffled B otherwise), with operand
+    copies rotated past the LLC."""
     from synth import bf16_matrix
     M, N, K = w.M, w.N, w.K
     print(f"bench: config {CONFIG_INDEX[w.name]} ({w.name}) {M}x{N}x{K}", file=sys.stderr,

@@ -1,6 +1,9 @@
 // Block-scaled MXFP4 x MXFP4 GEMM (TN) for few rows of A: decode-shaped
 // problems such as M = 32 against a large N x K weight, where the work is
-// streaming B from HBM once and the MFMAs are nearly idle.
+// streaming B from HBM once and the MFMAs are nearly idle. mxfp4_gemm also
+// runs it for problems of at most CUs / 8 tiles of 256 x 256, whose 32 x 32
+// tiles here spread over the whole chip where the tile kernel would keep
+// most CUs idle.
 //
 // Same contract and arithmetic as the tile kernel (the MXFP4 hipBLASLt path
 // of "Integrate MXFP4 hipblaslt GEMM support", ROCm/TransformerEngine #697,

@@ -4,7 +4,10 @@
 //     runs at (s_memtime against the 100 MHz s_memrealtime);
 //   * the same MFMA stream with the tile GEMM's LDS operand reads
 //     interleaved (8 ds_read_b128 per 16 MFMAs for 128 x 128 wave tiles, 6
-//     per 8 for 128 x 64 wave tiles at two waves per SIMD);
+//     per 8 for 128 x 64 wave tiles at two waves per SIMD), in the
+//     compiler's order or in a fixed order (ORDER, sched_group_barrier):
+//     per four MFMAs, MFMA read MFMA read MFMA MFMA (the tile GEMM's K
+//     loop), MFMA MFMA read twice, or MFMA read read MFMA MFMA MFMA;
 //   * LDS read bandwidth (ds_read_b128 only).
 // One workgroup per CU (96 KiB of dynamic LDS each); every LDS access stays
 // in the first 64 KiB; loops have fixed trip counts. Prints one JSON object
@@ -35,9 +38,34 @@ __device__ __forceinline__ v16f mfma(const uint4& x, const uint4& y, v16f c, uin
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(xv, yv, c, 4, 4, 0, (int)s, 0, (int)s);
 }
 
+// Instruction order of one half iteration (16 MFMAs, 8 reads) for ORDER
+// 1..3; 0 leaves it to the compiler.
+template <int ORDER>
+__device__ __forceinline__ void order16() {
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    if constexpr (ORDER == 1) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    } else if constexpr (ORDER == 2) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    } else if constexpr (ORDER == 3) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+    }
+  }
+}
+
 // Per K slice: NA A and NB B fragments (1 KiB each, contiguous) read from
 // LDS when READS, NA * NB MFMAs on the previous slice's fragments when MFMA.
-template <int NA, int NB, bool READS, bool MFMA, int WAVES>
+template <int NA, int NB, bool READS, bool MFMA, int WAVES, int ORDER = 0>
 __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(WAVES / 4, WAVES / 4)))
 void probe(uint64_t* out, float* sink, int iters) {
   extern __shared__ uint4 lds[];
@@ -66,6 +94,7 @@ void probe(uint64_t* out, float* sink, int iters) {
       for (int a = 0; a < NA; ++a)
 #pragma unroll
         for (int b = 0; b < NB; ++b) acc[a][b] = mfma(f0[NA + b], f0[a], acc[a][b], sc);
+      if constexpr (ORDER != 0) order16<ORDER>();
     }
 #pragma unroll
     for (int q = 0; q < NA + NB; ++q)
@@ -75,6 +104,7 @@ void probe(uint64_t* out, float* sink, int iters) {
       for (int a = 0; a < NA; ++a)
 #pragma unroll
         for (int b = 0; b < NB; ++b) acc[a][b] = mfma(f1[NA + b], f1[a], acc[a][b], sc);
+      if constexpr (ORDER != 0) order16<ORDER>();
     } else {
 #pragma unroll
       for (int q = 0; q < NA + NB; ++q) acc[0][0][q & 15] += (float)(f0[q].x ^ f1[q].y);
@@ -97,9 +127,9 @@ void probe(uint64_t* out, float* sink, int iters) {
   }
 }
 
-template <int NA, int NB, bool READS, bool MFMA, int WAVES>
+template <int NA, int NB, bool READS, bool MFMA, int WAVES, int ORDER = 0>
 int run(const char* name, int iters, int grid) {
-  auto k = probe<NA, NB, READS, MFMA, WAVES>;
+  auto k = probe<NA, NB, READS, MFMA, WAVES, ORDER>;
   CHECK(hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize,
                             96 * 1024));
   const int nw = grid * WAVES;
@@ -155,6 +185,9 @@ int main() {
   r |= run<4, 4, false, true, 4>("mfma only, 128x128 wave tiles", 8000, cus);
   r |= run<4, 2, false, true, 8>("mfma only, 128x64 wave tiles", 8000, cus);
   r |= run<4, 4, true, true, 4>("mfma + 8 LDS reads per 16 mfma", 8000, cus);
+  r |= run<4, 4, true, true, 4, 1>("mfma + 8 LDS reads per 16 mfma, M r M r M M", 8000, cus);
+  r |= run<4, 4, true, true, 4, 2>("mfma + 8 LDS reads per 16 mfma, M M r M M r", 8000, cus);
+  r |= run<4, 4, true, true, 4, 3>("mfma + 8 LDS reads per 16 mfma, M r r M M M", 8000, cus);
   r |= run<4, 2, true, true, 8>("mfma + 6 LDS reads per 8 mfma", 8000, cus);
   r |= run<4, 4, true, false, 4>("LDS reads only", 8000, cus);
   r |= run<4, 4, true, false, 16>("LDS reads only", 8000, cus);
