@@ -83,6 +83,9 @@ def parse():
     p.add_argument("--probe", action="store_true",
                    help="only run the MFMA / LDS microbenchmark (built by build.build_probe) "
                         "and print its cases as one JSON line")
+    p.add_argument("--sections", action="store_true",
+                   help="only run the tile GEMM's section timing (built by "
+                        "build.build_sections) and print its workloads as one JSON line")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="only run a plain device copy of this many MiB three times and exit "
                         "(the known-size kernel that scales the FETCH_SIZE/WRITE_SIZE counters)")
@@ -124,6 +127,22 @@ def copy_calibration(mib):
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}), flush=True)
+
+
+def run_sections():
+    """The tile GEMM's section timing in a child process: per section of the
+    kernel (K loop, step waits and barriers, epilogue parts) the mean cycles
+    per wave and tile, on the tile-GEMM workloads."""
+    import subprocess
+    exe = os.path.join(ROOT, "block_scaled_microscaling_amd", "gemm_sections")
+    if not os.path.exists(exe):
+        raise RuntimeError(f"{exe} is missing: build it with build.build_sections()")
+    res = subprocess.run([exe], capture_output=True, text=True, timeout=300)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError(f"gemm_sections failed with status {res.returncode}")
+    cases = [json.loads(line) for line in res.stdout.splitlines() if line.startswith("{")]
+    print(json.dumps({"sections": cases}), flush=True)
 
 
 def run_probe():
@@ -407,6 +426,9 @@ def main():
         return
     if args.probe:
         run_probe()
+        return
+    if args.sections:
+        run_sections()
         return
 
     import torch

@@ -95,6 +95,27 @@ def build_probe(out=PROBE_BIN, verbose=True):
     return str(out)
 
 
+# Section timing of the tile GEMM (probe/gemm_sections.hip): a standalone
+# executable that includes csrc/gemm.hip with its section timers switched on,
+# run by `python bench.py --sections`.
+SECTIONS_SRC = os.path.join(HERE, "probe", "gemm_sections.hip")
+SECTIONS_BIN = os.path.join(HERE, "gemm_sections")
+
+
+def build_sections(out=SECTIONS_BIN, verbose=True):
+    hipcc = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")
+    cmd = [hipcc, f"--offload-arch={ARCH}", "-O3", "-std=c++17",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-Wno-unused-command-line-argument", "-Wno-inline-asm", "-o", str(out), SECTIONS_SRC]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr + "\n")
+        raise subprocess.CalledProcessError(res.returncode, cmd)
+    return str(out)
+
+
 # Host-only AddressSanitizer: the device code is built as usual and the host
 # code (the C ABI's argument checks, launchers, per-device state) is
 # instrumented. Loading the result needs the matching runtime preloaded

@@ -90,6 +90,32 @@ constexpr int kEpiBf16 = 0;
 constexpr int kEpiFp32 = 1;
 constexpr int kEpiSwiglu = 2;
 
+// Section timers. In the library SectionTimer does nothing and its calls
+// compile to no code. A profiling build (probe/gemm_sections.hip) defines
+// MXFP4_SECTION_TIMERS and its own SectionTimer before including this file:
+// each wave then adds the s_memtime cycles since its previous mark to the
+// section a mark ends, and stores its sums once at the end of the kernel.
+enum Section {
+  kSecTileWait,     // a tile's first wait: its head loads landed, all waves met
+  kSecLoop,         // K loop: MFMAs, fragment reads and load issue, up to each step's wait
+  kSecDataWait,     // a step's wait for its next step's loads (and LDS reads)
+  kSecBarrier,      // a step's barrier after that wait
+  kSecLoopEnd,      // the last step's phase 3 and the wait after the loop
+  kSecEpiHead,      // next tile's context and head loads
+  kSecEpiStore,     // C (or the SwiGLU activation) parked and stored
+  kSecEpiBarrier,   // the wait and barrier after the stores
+  kSecEpiTail,      // next tile's tail loads
+  kNumSections
+};
+#ifndef MXFP4_SECTION_TIMERS
+struct SectionTimer {
+  __device__ void start() {}
+  template <int kSec>
+  __device__ void mark() {}
+  __device__ void store(int) {}
+};
+#endif
+
 // Scale chunks: kChunk half-steps (128 K each) of scale words for the 256
 // rows of an operand, laid out [half][r][half-step'][tile] for row
 // 128 half + 32 tile + r, where half-step' = half-step ^ ((r >> 1) & 7): the
@@ -367,8 +393,18 @@ __device__ __forceinline__ void mma_row(v16f_t (&acc)[4][4], const Frags& f, con
 
 // Wait for every load this wave issued and for its LDS reads, then meet the
 // other waves. The memory clobber keeps LDS accesses on their side.
-__device__ __forceinline__ void step_barrier() {
+// The profiling build times the wait and the barrier apart (two asm
+// statements); in the library they stay one statement, as scheduled.
+__device__ __forceinline__ void step_barrier(SectionTimer& st) {
+#ifdef MXFP4_SECTION_TIMERS
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+  st.mark<kSecDataWait>();
+  asm volatile("s_barrier" ::: "memory");
+  st.mark<kSecBarrier>();
+#else
+  (void)st;
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#endif
 }
 
 #define MXFP4_FENCE() __builtin_amdgcn_sched_barrier(0)
@@ -400,7 +436,7 @@ template <bool kFull, bool kGlu, bool kShufB, int P, int S>
 __device__ __forceinline__ void k_step(const Ctx& c0, Tiles& tl,
                                        uint8_t (*chunks)[2 * kChunkBytes], v16f_t (&acc)[4][4],
                                        Frags& fa, Frags& fb, HalfScales& sc0, HalfScales& sc1,
-                                       int T) {
+                                       int T, SectionTimer& st) {
   // Re-derive the per-lane offsets from opaque copies each step, so that the
   // compiler recomputes the addresses built on them instead of holding every
   // one of them in a register across the loop.
@@ -465,7 +501,8 @@ __device__ __forceinline__ void k_step(const Ctx& c0, Tiles& tl,
   read_frag_a<S>(c, tl, 3, 2, fb.a[2]);
   read_frag_a<S>(c, tl, 3, 3, fb.a[3]);
   group_end<2>();
-  step_barrier();
+  st.mark<kSecLoop>();
+  step_barrier(st);
   MXFP4_FENCE();
   // Phase 3: slice 3; read slice 0 and the scales of step T+1.
   const int ka = phys_step(c, min(T + 2, c.klast));
@@ -899,6 +936,8 @@ void gemm_tile_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__
   // FP32, masked lanes dropped by the store resource) between the head and
   // the tail loads of this tile.
   bool whole_prev = false;
+  SectionTimer st;
+  st.start();
   for (; p < total; p += gridDim.x) {
     // Wait for the head loads (vector memory operations complete in issue
     // order): outstanding may remain the 8 tail loads and, after a previous
@@ -911,6 +950,7 @@ void gemm_tile_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__
       asm volatile("s_waitcnt vmcnt(63)\n\ts_barrier" ::: "memory");
     else
       asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+    st.mark<kSecTileWait>();
 
     v16f_t acc[4][4];
 #pragma unroll
@@ -928,17 +968,18 @@ void gemm_tile_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__
 
     int T = 0;
     for (; T + 4 <= ksteps; T += 4) {
-      k_step<kFull, kGlu, kShufB, 1, 0>(c, tl, chunks, acc, fa, fb, sc0, sc1, T);
-      k_step<kFull, kGlu, kShufB, 2, 1>(c, tl, chunks, acc, fa, fb, sc0, sc1, T + 1);
-      k_step<kFull, kGlu, kShufB, 3, 0>(c, tl, chunks, acc, fa, fb, sc0, sc1, T + 2);
-      k_step<kFull, kGlu, kShufB, 0, 1>(c, tl, chunks, acc, fa, fb, sc0, sc1, T + 3);
+      k_step<kFull, kGlu, kShufB, 1, 0>(c, tl, chunks, acc, fa, fb, sc0, sc1, T, st);
+      k_step<kFull, kGlu, kShufB, 2, 1>(c, tl, chunks, acc, fa, fb, sc0, sc1, T + 1, st);
+      k_step<kFull, kGlu, kShufB, 3, 0>(c, tl, chunks, acc, fa, fb, sc0, sc1, T + 2, st);
+      k_step<kFull, kGlu, kShufB, 0, 1>(c, tl, chunks, acc, fa, fb, sc0, sc1, T + 3, st);
     }
-    if (T < ksteps) k_step<kFull, kGlu, kShufB, 1, 0>(c, tl, chunks, acc, fa, fb, sc0, sc1, T);
-    if (T + 1 < ksteps) k_step<kFull, kGlu, kShufB, 2, 1>(c, tl, chunks, acc, fa, fb, sc0, sc1, T + 1);
-    if (T + 2 < ksteps) k_step<kFull, kGlu, kShufB, 3, 0>(c, tl, chunks, acc, fa, fb, sc0, sc1, T + 2);
+    if (T < ksteps) k_step<kFull, kGlu, kShufB, 1, 0>(c, tl, chunks, acc, fa, fb, sc0, sc1, T, st);
+    if (T + 1 < ksteps) k_step<kFull, kGlu, kShufB, 2, 1>(c, tl, chunks, acc, fa, fb, sc0, sc1, T + 1, st);
+    if (T + 2 < ksteps) k_step<kFull, kGlu, kShufB, 3, 0>(c, tl, chunks, acc, fa, fb, sc0, sc1, T + 2, st);
     // Every load of this tile has landed and every LDS read has returned,
     // in all waves, before the next tile's loads reuse the buffers.
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    st.mark<kSecLoopEnd>();
 
     // Start the next tile's loads, then write this tile's C while they fly;
     // the last 8 loads issued are the ones the next wait leaves outstanding.
@@ -951,9 +992,11 @@ void gemm_tile_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__
         set_tile<kGlu, kShufB>(c, pn, tiles_m, tiles_n);
         issue_tile_head<kFull, kGlu, kShufB>(c, tl, chunks);
       }
+      st.mark<kSecEpiHead>();
       uint8_t* region = wave < 2 ? tl.a[1] + 16384 * wave : tl.b[1] + 16384 * (wave - 2);
       store_tile_swiglu(row0, col0, M, Nh, acc, wy, wx, lane, region, act_codes, act_scales,
                         static_cast<uint16_t*>(C));
+      st.mark<kSecEpiStore>();
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     } else if constexpr (kOutFp32) {
       // As for BF16 C: head loads first, C parked in slot 1 four rounds of
@@ -966,8 +1009,10 @@ void gemm_tile_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__
         set_tile<kGlu, kShufB>(c, pn, tiles_m, tiles_n);
         issue_tile_head<kFull, kGlu, kShufB>(c, tl, chunks);
       }
+      st.mark<kSecEpiHead>();
       uint8_t* region = wave < 2 ? tl.a[1] + 16384 * wave : tl.b[1] + 16384 * (wave - 2);
       store_tile_f32_lds(cur_tile, acc, wy, wx, lane, region, C);
+      st.mark<kSecEpiStore>();
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     } else {
       // The next tile's head loads (slot 0, chunks[0]) go out before the C
@@ -980,13 +1025,18 @@ void gemm_tile_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__
         set_tile<kGlu, kShufB>(c, pn, tiles_m, tiles_n);
         issue_tile_head<kFull, kGlu, kShufB>(c, tl, chunks);
       }
+      st.mark<kSecEpiHead>();
       uint8_t* region = wave < 2 ? tl.a[1] + 16384 * wave : tl.b[1] + 16384 * (wave - 2);
       store_tile_bf16_lds(cur_tile, acc, wy, wx, lane, region, C);
+      st.mark<kSecEpiStore>();
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     }
+    st.mark<kSecEpiBarrier>();
     if (pn < total) issue_tile_tail<kFull, kGlu, kShufB>(c, tl, chunks);
+    st.mark<kSecEpiTail>();
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  st.store(blockIdx.x * (kThreads / 64) + wave);
 }
 
 }  // namespace
