@@ -172,7 +172,8 @@ struct Ctx {
   int b_scale_blk;        // pre-shuffled B: first scale block of this tile
   uint32_t lane16;        // 16 * lane
   int klast, hlast;
-  int rot, rot_chunks;    // K rotation of this workgroup's XCD: K steps (multiple of 4), chunks
+  int rot, rot_chunks;    // K rotation of this tile: K steps (multiple of 4), chunks
+  int rot_xcd;            // K rotation of this workgroup's XCD (-1: none)
   uint32_t code_lane[2];  // per-lane code DMA offset for row groups at 16 r, 16 r + 8
   const uint8_t* tile_a;  // wave-uniform code bases of this tile, less kDmaBias
   const uint8_t* tile_b;
@@ -193,12 +194,18 @@ struct Ctx {
 };
 
 // Logical K step T (and 1024-K scale chunk) -> the step (chunk) loaded: the
-// K loop of every workgroup of one XCD starts rot steps into K and wraps
-// around. Cold operands: the 8 XCDs running tiles of one B panel row then
-// read different parts of it at any moment, so each part comes from HBM for
-// the first XCD only and from the last-level cache for the other seven,
-// instead of all eight waiting on HBM together. rot is 0 unless K % 1024 ==
-// 0, and a multiple of 4 steps, so scale chunks stay whole.
+// K loop of a tile starts rot steps into K and wraps around. rot is its XCD's
+// offset (XCD x starts x K / 8 in): the 8 XCDs running tiles of one B panel
+// row then read different parts of it at any moment, so each part comes from
+// HBM for the first XCD only and from the last-level cache for the other
+// seven, instead of all eight waiting on HBM together. Plain GEMM tiles add 4
+// steps where tile row + tile column is odd: of the tiles sharing an A or B
+// panel on one XCD, half then run 4 steps behind the others and find the
+// panel's lines in L2 (8192^3: the step's wait for its loads 180 -> 158
+// cycles, the epilogue 14.1k -> 12.0k cycles per tile, 2.3% faster; the
+// SwiGLU tiles, whose B rows come in gate/up halves, gained nothing and keep
+// the XCD offset alone). rot is 0 unless K % 1024 == 0, and a multiple of 4
+// steps, so scale chunks stay whole.
 __device__ __forceinline__ int phys_step(const Ctx& c, int t) {
   const int p = t + c.rot;
   return p >= c.ksteps ? p - c.ksteps : p;
@@ -583,6 +590,14 @@ template <bool kGlu, bool kShufB>
 __device__ __forceinline__ void set_tile(Ctx& c, int p, int tiles_m, int tiles_n) {
   int tm, tn;
   tile_of(p, tiles_m, tiles_n, tm, tn);
+  if constexpr (!kGlu) {
+    if (c.rot_xcd >= 0) {
+      int r = c.rot_xcd + 4 * ((tm + tn) & 1);
+      if (r >= c.ksteps) r -= c.ksteps;
+      c.rot = r;
+      c.rot_chunks = r / kChunkSteps;
+    }
+  }
   c.row0 = tm * kTileM;
   c.col0 = tn * (kGlu ? kTileN / 2 : kTileN);
   // Wave's first code row, clamped like the rows of its loads: rows past M
@@ -902,6 +917,7 @@ void gemm_tile_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__
   c.hlast = 2 * ksteps - 1;
   c.rot = kFull ? (((int)(blockIdx.x % kNumXcd) * ksteps) / kNumXcd) & ~3 : 0;
   c.rot_chunks = c.rot / kChunkSteps;
+  c.rot_xcd = kFull ? c.rot : -1;
   c.wave = wave;
   c.interior = false;
 #pragma unroll
