@@ -284,43 +284,16 @@ __device__ __forceinline__ void load_b2(const Ctx& c, Tiles& t, int kt) {
                m0);
 }
 
-// Scale part u (0..7) of operand X (0 = A, 1 = B) of chunk `chunk`: words
-// q = 256 u + 64 w + lane of the chunk: tile = lane % 4, half-step' =
-// (lane / 4) % 8, r = 8 (u % 4) + 2 w + lane / 32, half = u / 4, so
-// row = 128 (u / 4) + 32 (lane % 4) + 8 (u % 4) + 2 w + lane / 32 and the
-// XOR key (r >> 1) & 7 = 4 (u % 2) + w.
-template <bool kGlu, bool kShufB, int X, int U>
-__device__ __forceinline__ void load_scale_part(const Ctx& c, uint8_t* buf, int chunk) {
-  if constexpr (kShufB && X == 1) {
-    // The shuffled scale block is the LDS chunk image: part U of wave w is
-    // bytes 1024 U + 256 w + 4 lane of it.
-    const int chunk_c = phys_chunk(c, min(chunk, c.nchunks - 1));
-    const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(buf) + kChunkBytes +
-                                                        4 * (256 * U + 64 * c.wave));
-    dma4(c.Bs + (int64_t)(c.b_scale_blk + chunk_c) * kChunkBytes + 1024 * U + 256 * c.wave +
-             (c.lane16 >> 2),
-         dst);
-    return;
-  }
-  const uint8_t* base = X == 0 ? c.As : c.Bs;
-  const int t_row = 128 * (U / 4) + 8 * (U % 4) + 2 * c.wave + c.scale_lane;
-  const int row = X == 0 ? min(c.row0 + t_row, c.M - 1) : b_row<kGlu>(c, t_row);
-  const int t = c.scale_t ^ (4 * (U % 2) + c.wave);
-  // With a rotation every chunk is whole (K % 1024 == 0).
-  const int hs = c.rot ? kChunk * phys_chunk(c, min(chunk, c.nchunks - 1)) + t
-                       : min(kChunk * chunk + t, c.hlast);
-  const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(buf) + X * kChunkBytes +
-                                                      4 * (256 * U + 64 * c.wave));
-  dma4(base + (int64_t)row * c.scale_row_bytes + hs * 4, dst);
-}
-
-// Scale parts 2p, 2p + 1 of operand X for chunk `chunk` as one DMA pair:
-// their words sit 1024 bytes apart in the chunk buffer, and their per-lane
-// offsets (prepared per tile, with kScaleBias) are relative to part 2p's
-// clamped base row. Only for chunks whose 8 half-steps all lie within K; the
-// last chunk of a K that is not a multiple of 1024 takes load_scale_part.
+// Scale part u (0..7) of operand X (0 = A, 1 = B) of a chunk is its words
+// q = 256 u + 64 w + lane: tile = lane % 4, half-step' = (lane / 4) % 8,
+// r = 8 (u % 4) + 2 w + lane / 32, half = u / 4, so the lane's row is
+// 128 (u / 4) + 32 (lane % 4) + 8 (u % 4) + 2 w + lane / 32 and the XOR key
+// (r >> 1) & 7 = 4 (u % 2) + w. Parts 2p, 2p + 1 go as one DMA pair: their
+// words sit 1024 bytes apart in the chunk buffer, and their per-lane offsets
+// (prepared per tile, with kScaleBias) are relative to part 2p's clamped
+// base row. kClampK (K not a multiple of 1024): the last chunk ends past K.
 constexpr int kScaleBias = 1024;
-template <bool kGlu, bool kShufB, int X, int PP>
+template <bool kGlu, bool kShufB, int X, int PP, bool kClampK>
 __device__ __forceinline__ void load_scale_pair(const Ctx& c, uint8_t* buf, int chunk) {
   const uint8_t* base = X == 0 ? c.As : c.Bs;
   // The last steps prefetch chunks past the end of K: those re-read the last
@@ -339,11 +312,20 @@ __device__ __forceinline__ void load_scale_pair(const Ctx& c, uint8_t* buf, int 
   }
   const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr(buf) + X * kChunkBytes +
                                                      4 * (256 * (2 * PP) + 64 * c.wave));
+  uint32_t o0 = c.soff[X][PP][0], o1 = c.soff[X][PP][1];
+  if constexpr (kClampK) {
+    // The chunk may end past K: a lane whose half-step t lies past the last
+    // one (tl) reads half-step tl instead (4 (t - tl) bytes back), so no
+    // lane reads past its row, and past the scale array at its last row.
+    const int tl = c.hlast - kChunk * chunk_c;
+    o0 -= 4u * (uint32_t)max((c.scale_t ^ c.wave) - tl, 0);
+    o1 -= 4u * (uint32_t)max((c.scale_t ^ (4 + c.wave)) - tl, 0);
+  }
   asm volatile(
       "s_mov_b32 m0, %3\n\ts_nop 0\n\t"
       "global_load_lds_dword %0, %2\n\t"
       "global_load_lds_dword %1, %2 offset:1024"
-      :: "v"(c.soff[X][PP][0]), "v"(c.soff[X][PP][1]), "s"(sgpr_ptr(sbase)), "s"(m0)
+      :: "v"(o0), "v"(o1), "s"(sgpr_ptr(sbase)), "s"(m0)
       : "m0");
 }
 
@@ -351,12 +333,7 @@ __device__ __forceinline__ void load_scale_pair(const Ctx& c, uint8_t* buf, int 
 template <bool kFull, bool kGlu, bool kShufB, int X, int PP>
 __device__ __forceinline__ void load_scales2(const Ctx& c, uint8_t* buf, int chunk) {
   // Shuffled B scales are padded to whole chunks: always the pair form.
-  if constexpr (kFull || (kShufB && X == 1)) {
-    load_scale_pair<kGlu, kShufB, X, PP>(c, buf, chunk);
-  } else {
-    load_scale_part<kGlu, kShufB, X, 2 * PP>(c, buf, chunk);
-    load_scale_part<kGlu, kShufB, X, 2 * PP + 1>(c, buf, chunk);
-  }
+  load_scale_pair<kGlu, kShufB, X, PP, !kFull && !(kShufB && X == 1)>(c, buf, chunk);
 }
 
 // The lane's scale operands of half-step t (0..7) of a chunk buffer.
