@@ -26,8 +26,8 @@
 // bytes of A and B scales (one dword instruction each). Two steps are in
 // flight per wave (16 KiB), 128 KiB per workgroup: the LDS caps the bytes in
 // flight per CU, and with one workgroup per CU that caps the HBM rate
-// (11.0 us at 32 x 8192 x 8192 against 6.3 us for a plain 1024-workgroup
-// streaming read of B).
+// (10.9 us at 32 x 8192 x 8192, B's loads nontemporal, against 6.3 us for
+// a plain 1024-workgroup streaming read of B).
 //
 // Data movement, fragment-order operands (gemm_frag_kernel). A and B are
 // stored so that each MFMA operand is one contiguous 1 KiB; every load is a
@@ -77,11 +77,21 @@ struct Lanes {
   uint32_t scale;    // scale DMA: row lane / 2, dword lane % 2
 };
 
+// dma16 with the nontemporal hint: for B when a single tile row of A reads
+// it, so that each line is used once (32 x 8192 x 8192: 11.2 -> 10.9 us;
+// with several tile rows of A the other rows' workgroups then miss, 64 x
+// 8192 x 8192: 17.1 -> 19.8 us, so it is kept for one tile row only).
+__device__ __forceinline__ void dma16_nt(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
+               :: "v"(g), "s"(lds) : "m0");
+}
+
 // Issue the loads of K step `st` into the slot at LDS address `slot`.
 // Code instruction q fills tile rows 8 q .. 8 q + 7: lane i lands at row
 // 8 q + i / 8, physical chunk i % 8, and so fetches logical chunk
 // (i % 8) ^ swizzle(row). The scale instruction lands lane i's dword at
 // 4 i: [row][dword 0, 1].
+template <bool kNtB>
 __device__ __forceinline__ void issue_step(const uint8_t* a, const uint8_t* b, const uint8_t* as,
                                            const uint8_t* bs, int row_bytes, const Lanes& ln,
                                            uint32_t slot, int st) {
@@ -90,8 +100,13 @@ __device__ __forceinline__ void issue_step(const uint8_t* a, const uint8_t* b, c
   for (int q = 0; q < 4; ++q)
     dma16(a + (int64_t)(8 * q) * row_bytes + kb + ln.code[q & 1], slot + q * 1024);
 #pragma unroll
-  for (int q = 0; q < 4; ++q)
-    dma16(b + (int64_t)(8 * q) * row_bytes + kb + ln.code[q & 1], slot + kSlotB + q * 1024);
+  for (int q = 0; q < 4; ++q) {
+    const uint8_t* g = b + (int64_t)(8 * q) * row_bytes + kb + ln.code[q & 1];
+    if constexpr (kNtB)
+      dma16_nt(g, slot + kSlotB + q * 1024);
+    else
+      dma16(g, slot + kSlotB + q * 1024);
+  }
   dma4(as + st * kScaleRow + ln.scale, slot + kSlotAs);
   dma4(bs + st * kScaleRow + ln.scale, slot + kSlotBs);
 }
@@ -131,7 +146,7 @@ __device__ __forceinline__ void reduce_store(float* red, const v16f_t& acc, int 
   }
 }
 
-template <bool kOutFp32>
+template <bool kOutFp32, bool kNtB>
 __global__ __launch_bounds__(kThreads) void gemm_skinny_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ As,
     const uint8_t* __restrict__ B, const uint8_t* __restrict__ Bs, int N, int K,
@@ -173,8 +188,8 @@ __global__ __launch_bounds__(kThreads) void gemm_skinny_kernel(
   const int scale_off = r * kScaleRow + 4 * h;
 
   v16f_t acc = v16f_t{};
-  if (nst > 0) issue_step(a, b, as, bs, row_bytes, ln, ring_lds, wave);
-  if (nst > 1) issue_step(a, b, as, bs, row_bytes, ln, ring_lds + kSlotBytes, wave + kWaves);
+  if (nst > 0) issue_step<kNtB>(a, b, as, bs, row_bytes, ln, ring_lds, wave);
+  if (nst > 1) issue_step<kNtB>(a, b, as, bs, row_bytes, ln, ring_lds + kSlotBytes, wave + kWaves);
   for (int i = 0; i < nst; ++i) {
     // Step i has landed once at most the next step's loads are outstanding.
     if (i + 1 < nst)
@@ -194,7 +209,7 @@ __global__ __launch_bounds__(kThreads) void gemm_skinny_kernel(
     if (i + 2 < nst) {
       // The slot is refilled only after every read of it has returned.
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      issue_step(a, b, as, bs, row_bytes, ln, ring_lds + (i & 1) * kSlotBytes,
+      issue_step<kNtB>(a, b, as, bs, row_bytes, ln, ring_lds + (i & 1) * kSlotBytes,
                  wave + (i + 2) * kWaves);
     }
     acc = mfma_fp4<0, 0>(fb[0], fa[0], acc, sb, sa);
@@ -348,12 +363,22 @@ hipError_t launch_gemm_skinny(const void* A, const void* As, const void* B, cons
   const auto* as = static_cast<const uint8_t*>(As);
   const auto* b = static_cast<const uint8_t*>(B);
   const auto* bs = static_cast<const uint8_t*>(Bs);
-  if (out_fp32)
-    hipLaunchKernelGGL(gemm_skinny_kernel<true>, grid, dim3(kThreads), 0, stream, a, as, b, bs, N,
-                       K, C);
+  // One tile row of A: every line of B is read by one workgroup only. Short
+  // K (few steps per wave) measured slower with the hint (32 x 8192 x 1024:
+  // 3.50 -> 3.66 us), long K faster (32 x 28672 x 4096: 20.5 -> 20.2 us).
+  const bool nt_b = M == kTile && K >= 4096;
+  if (out_fp32 && nt_b)
+    hipLaunchKernelGGL((gemm_skinny_kernel<true, true>), grid, dim3(kThreads), 0, stream, a, as,
+                       b, bs, N, K, C);
+  else if (out_fp32)
+    hipLaunchKernelGGL((gemm_skinny_kernel<true, false>), grid, dim3(kThreads), 0, stream, a, as,
+                       b, bs, N, K, C);
+  else if (nt_b)
+    hipLaunchKernelGGL((gemm_skinny_kernel<false, true>), grid, dim3(kThreads), 0, stream, a, as,
+                       b, bs, N, K, C);
   else
-    hipLaunchKernelGGL(gemm_skinny_kernel<false>, grid, dim3(kThreads), 0, stream, a, as, b, bs,
-                       N, K, C);
+    hipLaunchKernelGGL((gemm_skinny_kernel<false, false>), grid, dim3(kThreads), 0, stream, a, as,
+                       b, bs, N, K, C);
   return hipGetLastError();
 }
 
