@@ -147,7 +147,7 @@ static int run(const Shape& s) {
   const int tiles_m = (s.M + 255) / 256;
   const int tiles_n = s.swiglu ? (s.N / 2 + 127) / 128 : (s.N + 255) / 256;
   const int total = tiles_m * tiles_n;
-  const int grid = total < workers ? total : workers;
+  const int grid = mxfp4::tile_grid(total, workers);
   const int ksteps = s.K / 256;
   double sum[mxfp4::kSlots] = {0};
   double tiles = 0;
