@@ -332,7 +332,7 @@ __device__ __forceinline__ void load_scale_pair(const Ctx& c, uint8_t* buf, int 
 // kFull: K is a multiple of 1024, so every chunk is whole.
 template <bool kFull, bool kGlu, bool kShufB, int X, int PP>
 __device__ __forceinline__ void load_scales2(const Ctx& c, uint8_t* buf, int chunk) {
-  // Shuffled B scales are padded to whole chunks: always the pair form.
+  // Shuffled B scales are padded to whole chunks, so they need no clamp.
   load_scale_pair<kGlu, kShufB, X, PP, !kFull && !(kShufB && X == 1)>(c, buf, chunk);
 }
 
