@@ -135,6 +135,31 @@ def test_random_operands_many_tiles(M, N, K, out_dtype, kernel):
     _assert_not_silent_zeros(out.float().cpu().numpy(), c_ref, s_ref)
 
 
+def _sweep_shapes(n=20, seed=20261203):
+    """Seeded shapes: M, N multiples of 32 up to 768, K a multiple of 256 up
+    to 2048 (ragged tile edges, one or several K steps and scale chunks)."""
+    rng = np.random.default_rng(seed)
+    return [(32 * int(rng.integers(1, 25)), 32 * int(rng.integers(1, 25)),
+             256 * int(rng.integers(1, 9))) for _ in range(n)]
+
+
+@pytest.mark.parametrize("idx", range(20))
+def test_random_shape_sweep(idx):
+    """Seeded random shapes through both kernels (mxfp4_gemm: split-K for
+    these sizes; mxfp4_gemm_tile: the tile kernel with edge tiles), BF16 and
+    FP32 out alternating, against the oracle."""
+    M, N, K = _sweep_shapes()[idx]
+    out_dtype = torch.bfloat16 if idx % 2 == 0 else torch.float32
+    announce(f"gemm sweep {idx}: {M}x{N}x{K} {out_dtype}")
+    Ac, Bc = random_codes(M, K, 900 + idx), random_codes(N, K, 950 + idx)
+    As, Bs = random_scales(M, K, 1000 + idx), random_scales(N, K, 1050 + idx)
+    c_ref, s_ref = oracle.gemm(Ac, As, Bc, Bs)
+    for kernel in ("auto", "tile"):
+        out = _gemm(Ac, As, Bc, Bs, out_dtype, kernel)
+        check_gemm_output(out, c_ref, s_ref)
+        _assert_not_silent_zeros(out.float().cpu().numpy(), c_ref, s_ref)
+
+
 @pytest.mark.parametrize("N", [2048, 2080])
 def test_kernel_choice_boundary(N):
     """1024 x N: 4 x 8 = 32 tiles of 256 x 256 (CUs / 8 on a 256-CU part:
