@@ -6,12 +6,14 @@ marshals arguments. PyTorch supplies device memory and streams.
 
 Two layers, same names as the C ABI:
   * mxfp4_available, mxfp4_strerror, mxfp4_quantize, mxfp4_quantize_async,
-    mxfp4_quantize_2d, mxfp4_quantize_sr, mxfp4_quantize_2d_sr, mxfp4_gemm,
+    mxfp4_quantize_2d, mxfp4_quantize_sr, mxfp4_quantize_2d_sr,
+    mxfp4_quantize_sr_rows, mxfp4_quantize_2d_sr_rows, mxfp4_gemm,
     mxfp4_gemm_tile, mxfp4_gemm_swiglu, mxfp4_shuffle_b(_sizes), mxfp4_gemm_bshuffled,
     mxfp4_quantize_frag, mxfp4_to_frag, mxfp4_gemm_frag take raw device
     pointers (ints) and return the C status code.
-  * quantize(x), quantize_2d(x), quantize_sr(x, seed), quantize_2d_sr(x,
-    seed), gemm(...), gemm_tile(...) and gemm_swiglu(...) take torch tensors,
+  * quantize(x), quantize_2d(x), quantize_sr(x, seed, row0=0),
+    quantize_2d_sr(x, seed, row0=0), gemm(...), gemm_tile(...) and
+    gemm_swiglu(...) take torch tensors,
     check their dtype, device, shape and contiguity, allocate outputs when none
     are given, enqueue on torch's current stream and raise Mxfp4Error on a
     non-zero status.
@@ -25,7 +27,8 @@ import os
 __all__ = [
     "Mxfp4Error", "OUT_BF16", "OUT_FP32", "library_path", "load_library",
     "mxfp4_available", "mxfp4_strerror", "mxfp4_quantize", "mxfp4_quantize_async",
-    "mxfp4_quantize_2d", "mxfp4_quantize_sr", "mxfp4_quantize_2d_sr", "mxfp4_gemm",
+    "mxfp4_quantize_2d", "mxfp4_quantize_sr", "mxfp4_quantize_2d_sr", "mxfp4_quantize_sr_rows",
+    "mxfp4_quantize_2d_sr_rows", "mxfp4_gemm",
     "mxfp4_gemm_tile", "mxfp4_gemm_swiglu", "quantize", "quantize_2d", "quantize_sr",
     "quantize_2d_sr", "gemm", "gemm_tile",
     "gemm_swiglu", "mxfp4_shuffle_b_sizes", "mxfp4_shuffle_b", "mxfp4_gemm_bshuffled",
@@ -71,6 +74,10 @@ def load_library():
         lib.mxfp4_quantize_sr.restype = i32
         lib.mxfp4_quantize_2d_sr.argtypes = [vp, i64, i64, u64, vp, vp, vp, vp, vp]
         lib.mxfp4_quantize_2d_sr.restype = i32
+        lib.mxfp4_quantize_sr_rows.argtypes = [vp, i64, i64, i64, u64, vp, vp, vp]
+        lib.mxfp4_quantize_sr_rows.restype = i32
+        lib.mxfp4_quantize_2d_sr_rows.argtypes = [vp, i64, i64, i64, u64, vp, vp, vp, vp, vp]
+        lib.mxfp4_quantize_2d_sr_rows.restype = i32
         lib.mxfp4_gemm.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, vp, vp]
         lib.mxfp4_gemm.restype = i32
         lib.mxfp4_gemm_tile.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, vp, vp]
@@ -124,6 +131,18 @@ def mxfp4_quantize_2d_sr(x_bf16, M, K, seed, codes_row, scales_row, codes_col, s
                          stream):
     return int(load_library().mxfp4_quantize_2d_sr(x_bf16, M, K, seed, codes_row, scales_row,
                                                    codes_col, scales_col, stream))
+
+
+def mxfp4_quantize_sr_rows(x_bf16, M, K, row0, seed, codes_out, scales_out, stream):
+    return int(load_library().mxfp4_quantize_sr_rows(x_bf16, M, K, row0, seed, codes_out,
+                                                     scales_out, stream))
+
+
+def mxfp4_quantize_2d_sr_rows(x_bf16, M, K, row0, seed, codes_row, scales_row, codes_col,
+                              scales_col, stream):
+    return int(load_library().mxfp4_quantize_2d_sr_rows(x_bf16, M, K, row0, seed, codes_row,
+                                                        scales_row, codes_col, scales_col,
+                                                        stream))
 
 
 def mxfp4_gemm(A_codes, A_scales, B_codes, B_scales, M, N, K, out_dtype, C, stream):
@@ -245,9 +264,11 @@ def _seed(seed):
     return seed
 
 
-def quantize_sr(x, seed, codes=None, scales=None, stream=None):
+def quantize_sr(x, seed, codes=None, scales=None, stream=None, row0=0):
     """Row-wise BF16 -> MXFP4 with stochastic rounding (Philox4x32-10 keyed by
-    block coordinates and the 64-bit `seed`). x: bfloat16 [M, K] on the GPU.
+    block coordinates and the 64-bit `seed`). x: bfloat16 [M, K] on the GPU,
+    rows row0 .. row0 + M - 1 of a larger input (the draws key by those
+    global rows; row0 = 0 is the plain call).
 
     Returns (codes uint8 [M, K/2], scales uint8 [M, K/32]).
     """
@@ -262,15 +283,17 @@ def quantize_sr(x, seed, codes=None, scales=None, stream=None):
         scales = torch.empty((M, K // 32), dtype=torch.uint8, device=x.device)
     _check(codes, "codes", torch.uint8, (M, K // 2))
     _check(scales, "scales", torch.uint8, (M, K // 32))
-    rc = mxfp4_quantize_sr(x.data_ptr(), M, K, _seed(seed), codes.data_ptr(), scales.data_ptr(),
-                           _stream_handle(stream))
+    rc = mxfp4_quantize_sr_rows(x.data_ptr(), M, K, int(row0), _seed(seed), codes.data_ptr(),
+                                scales.data_ptr(), _stream_handle(stream))
     if rc != 0:
-        raise Mxfp4Error(rc, "mxfp4_quantize_sr")
+        raise Mxfp4Error(rc, "mxfp4_quantize_sr_rows")
     return codes, scales
 
 
-def quantize_2d_sr(x, seed, stream=None):
-    """Row-wise and column-wise BF16 -> MXFP4 with stochastic rounding.
+def quantize_2d_sr(x, seed, stream=None, row0=0):
+    """Row-wise and column-wise BF16 -> MXFP4 with stochastic rounding; x
+    may be rows row0 .. of a larger input (row0 % 32 == 0), whose global
+    rows and row blocks key the draws.
 
     Returns (codes [M, K/2], scales [M, K/32], codes_t [K, M/2], scales_t
     [K, M/32]), uint8.
@@ -285,11 +308,11 @@ def quantize_2d_sr(x, seed, stream=None):
     scales = torch.empty((M, K // 32), dtype=torch.uint8, device=dev)
     codes_t = torch.empty((K, M // 2), dtype=torch.uint8, device=dev)
     scales_t = torch.empty((K, M // 32), dtype=torch.uint8, device=dev)
-    rc = mxfp4_quantize_2d_sr(x.data_ptr(), M, K, _seed(seed), codes.data_ptr(),
-                              scales.data_ptr(), codes_t.data_ptr(), scales_t.data_ptr(),
-                              _stream_handle(stream))
+    rc = mxfp4_quantize_2d_sr_rows(x.data_ptr(), M, K, int(row0), _seed(seed), codes.data_ptr(),
+                                   scales.data_ptr(), codes_t.data_ptr(), scales_t.data_ptr(),
+                                   _stream_handle(stream))
     if rc != 0:
-        raise Mxfp4Error(rc, "mxfp4_quantize_2d_sr")
+        raise Mxfp4Error(rc, "mxfp4_quantize_2d_sr_rows")
     return codes, scales, codes_t, scales_t
 
 

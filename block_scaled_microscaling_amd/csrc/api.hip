@@ -151,32 +151,46 @@ int mxfp4_quantize_2d(const void* x_bf16, int64_t M, int64_t K, void* codes_row,
                                                  static_cast<hipStream_t>(stream)));
 }
 
-int mxfp4_quantize_sr(const void* x_bf16, int64_t M, int64_t K, uint64_t seed, void* codes_out,
-                      void* scales_out, void* stream) {
+int mxfp4_quantize_sr_rows(const void* x_bf16, int64_t M, int64_t K, int64_t row0, uint64_t seed,
+                           void* codes_out, void* scales_out, void* stream) {
   if (!x_bf16 || !codes_out || !scales_out) return MXFP4_EINVAL;
   if (M < 1 || K < 32 || K % 32 != 0 || M > kMaxDim || K > kMaxDim) return MXFP4_EINVAL;
+  if (row0 < 0 || row0 > kMaxDim - M) return MXFP4_EINVAL;
   if (M * K >= kMaxBytes) return MXFP4_EINVAL;
   if (!aligned(x_bf16, 16) || !aligned(codes_out, 4)) return MXFP4_EALIGN;
   const int dev = check_device();
   if (dev != MXFP4_OK) return dev;
-  return launch_status(mxfp4::launch_quantize_sr(x_bf16, M, K, seed, codes_out, scales_out,
-                                                 static_cast<hipStream_t>(stream)));
+  return launch_status(mxfp4::launch_quantize_sr(x_bf16, M, K, row0, seed, codes_out,
+                                                 scales_out, static_cast<hipStream_t>(stream)));
 }
 
-int mxfp4_quantize_2d_sr(const void* x_bf16, int64_t M, int64_t K, uint64_t seed,
-                         void* codes_row, void* scales_row, void* codes_col, void* scales_col,
-                         void* stream) {
+int mxfp4_quantize_sr(const void* x_bf16, int64_t M, int64_t K, uint64_t seed, void* codes_out,
+                      void* scales_out, void* stream) {
+  return mxfp4_quantize_sr_rows(x_bf16, M, K, 0, seed, codes_out, scales_out, stream);
+}
+
+int mxfp4_quantize_2d_sr_rows(const void* x_bf16, int64_t M, int64_t K, int64_t row0,
+                              uint64_t seed, void* codes_row, void* scales_row, void* codes_col,
+                              void* scales_col, void* stream) {
   if (!x_bf16 || !codes_row || !scales_row || !codes_col || !scales_col) return MXFP4_EINVAL;
   if (M < 32 || K < 32 || M % 32 != 0 || K % 32 != 0 || M > kMaxDim || K > kMaxDim)
     return MXFP4_EINVAL;
+  if (row0 < 0 || row0 % 32 != 0 || row0 > kMaxDim - M) return MXFP4_EINVAL;
   if (M * K >= kMaxBytes) return MXFP4_EINVAL;
   if (!aligned(x_bf16, 16) || !aligned(codes_row, 16) || !aligned(codes_col, 16))
     return MXFP4_EALIGN;
   const int dev = check_device();
   if (dev != MXFP4_OK) return dev;
-  return launch_status(mxfp4::launch_quantize_2d_sr(x_bf16, (int)M, (int)K, seed, codes_row,
-                                                    scales_row, codes_col, scales_col,
+  return launch_status(mxfp4::launch_quantize_2d_sr(x_bf16, (int)M, (int)K, row0, seed,
+                                                    codes_row, scales_row, codes_col, scales_col,
                                                     static_cast<hipStream_t>(stream)));
+}
+
+int mxfp4_quantize_2d_sr(const void* x_bf16, int64_t M, int64_t K, uint64_t seed,
+                         void* codes_row, void* scales_row, void* codes_col, void* scales_col,
+                         void* stream) {
+  return mxfp4_quantize_2d_sr_rows(x_bf16, M, K, 0, seed, codes_row, scales_row, codes_col,
+                                   scales_col, stream);
 }
 
 int mxfp4_gemm(const void* A_codes, const void* A_scales, const void* B_codes,

@@ -19,11 +19,14 @@ hipError_t launch_quantize_2d(const void* x_bf16, int M, int K, void* codes_row,
 
 // Stochastic-rounding variants (Philox4x32-10 keyed by block coordinates,
 // direction and `seed`): row-wise over [M, K], and both forms of X [M, K].
-hipError_t launch_quantize_sr(const void* x_bf16, int64_t M, int64_t K, uint64_t seed,
-                              void* codes, void* scales, hipStream_t stream);
-hipError_t launch_quantize_2d_sr(const void* x_bf16, int M, int K, uint64_t seed, void* codes_row,
-                                 void* scales_row, void* codes_col, void* scales_col,
-                                 hipStream_t stream);
+// The input holds rows row0 .. row0 + M - 1 of a larger one; the draws are
+// keyed by those global rows (and, column-wise, by the global row block
+// row0 / 32 + j; row0 % 32 == 0 there).
+hipError_t launch_quantize_sr(const void* x_bf16, int64_t M, int64_t K, int64_t row0,
+                              uint64_t seed, void* codes, void* scales, hipStream_t stream);
+hipError_t launch_quantize_2d_sr(const void* x_bf16, int M, int K, int64_t row0, uint64_t seed,
+                                 void* codes_row, void* scales_row, void* codes_col,
+                                 void* scales_col, hipStream_t stream);
 
 // C[M,N] = A[M,K] * B[N,K]^T with block scales; out_fp32 selects FP32 vs BF16.
 hipError_t launch_gemm(const void* A, const void* As, const void* B, const void* Bs, int M,

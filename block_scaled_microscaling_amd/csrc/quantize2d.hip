@@ -35,7 +35,10 @@
 // lane draws for load 2g, the odd lane for 2g + 1, one DPP swap). Column
 // phase: each thread owns whole column blocks and takes both draws of each,
 // keyed with direction 1, the column of X as the row and the block index
-// along M as the block column.
+// along M as the block column. Both directions key by global coordinates:
+// the input may be rows row0 .. row0 + M - 1 of a larger X (row0 % 32 == 0),
+// whose rows and row blocks the draws then take, so that a row shard's
+// outputs are the corresponding part of the whole input's.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -149,7 +152,8 @@ template <bool kSR, int kC, int kRB>
 __global__ __launch_bounds__((Geom<kC, kRB>::kThreads)) void quantize_2d_kernel(
     const uint8_t* __restrict__ x, int M, int K, uint8_t* __restrict__ codes_row,
     uint8_t* __restrict__ scales_row, uint8_t* __restrict__ codes_col,
-    uint8_t* __restrict__ scales_col, uint32_t key0, uint32_t key1, bool xcd_regions) {
+    uint8_t* __restrict__ scales_col, uint32_t row0, uint32_t key0, uint32_t key1,
+    bool xcd_regions) {
   using G = Geom<kC, kRB>;
   constexpr int kCols = kC;
   constexpr int kThreads = G::kThreads;
@@ -195,7 +199,7 @@ __global__ __launch_bounds__((Geom<kC, kRB>::kThreads)) void quantize_2d_kernel(
           // Draws for the pair of loads (i, i + 1), taken at the even one.
           uint32_t rnd[2];
           if ((i & 1) == 0) {
-            const uint32_t drow = (uint32_t)(m0 + kRpl * (i + odd) + t / kSeg);
+            const uint32_t drow = row0 + (uint32_t)(m0 + kRpl * (i + odd) + t / kSeg);
             const Draw d = philox4x32_10((uint32_t)(col / 32), drow, kDirRowwise,
                                          (uint32_t)((t >> 1) & 1), key0, key1);
             const uint32_t got0 = swap_pair(odd ? d.w[0] : d.w[2]);
@@ -251,10 +255,11 @@ __global__ __launch_bounds__((Geom<kC, kRB>::kThreads)) void quantize_2d_kernel(
       for (int e = 0; e < 2; ++e) {
         const uint32_t byte = scale_byte(e == 0 ? (uint32_t)mx.x : (uint32_t)mx.y);
         if constexpr (kSR) {
-          // Block (column c0 + 2 cp + e of X, row block m0 / 32 + rb): draw h
+          // Block (column c0 + 2 cp + e of X, global row block row0 / 32 +
+          // m0 / 32 + rb): draw h
           // covers its rows 16 h .. 16 h + 15.
           const uint32_t kcol = (uint32_t)(c0 + 2 * cp + e);
-          const uint32_t jblk = (uint32_t)(m0 / 32 + rb);
+          const uint32_t jblk = row0 / 32 + (uint32_t)(m0 / 32 + rb);
           const Draw d[2] = {philox4x32_10(jblk, kcol, kDirColumnwise, 0u, key0, key1),
                              philox4x32_10(jblk, kcol, kDirColumnwise, 1u, key0, key1)};
 #pragma unroll
@@ -378,13 +383,13 @@ hipError_t launch_quantize_2d(const void* x_bf16, int M, int K, void* codes_row,
                      stream, static_cast<const uint8_t*>(x_bf16), M, K,
                      static_cast<uint8_t*>(codes_row), static_cast<uint8_t*>(scales_row),
                      static_cast<uint8_t*>(codes_col), static_cast<uint8_t*>(scales_col), 0u, 0u,
-                     true);
+                     0u, true);
   return hipGetLastError();
 }
 
-hipError_t launch_quantize_2d_sr(const void* x_bf16, int M, int K, uint64_t seed, void* codes_row,
-                                 void* scales_row, void* codes_col, void* scales_col,
-                                 hipStream_t stream) {
+hipError_t launch_quantize_2d_sr(const void* x_bf16, int M, int K, int64_t row0, uint64_t seed,
+                                 void* codes_row, void* scales_row, void* codes_col,
+                                 void* scales_col, hipStream_t stream) {
   dim3 grid;
   const hipError_t e = grid_2d(M, K, kColsSr, false, grid);
   if (e != hipSuccess) return e;
@@ -393,7 +398,7 @@ hipError_t launch_quantize_2d_sr(const void* x_bf16, int M, int K, uint64_t seed
                      stream, static_cast<const uint8_t*>(x_bf16), M, K,
                      static_cast<uint8_t*>(codes_row), static_cast<uint8_t*>(scales_row),
                      static_cast<uint8_t*>(codes_col), static_cast<uint8_t*>(scales_col),
-                     (uint32_t)seed, (uint32_t)(seed >> 32), false);
+                     (uint32_t)row0, (uint32_t)seed, (uint32_t)(seed >> 32), false);
   return hipGetLastError();
 }
 

@@ -3,7 +3,8 @@
 // Same block arithmetic as quantize.hip for the scale (integer amax of the
 // BF16 bits, scale byte = max(E_field(amax) - 2, 0)); the codes round
 // stochastically with one Philox4x32-10 draw per 16-element half block,
-// keyed by (block column, row, direction 0, half) as stochastic.h describes.
+// keyed by (block column, row, direction 0, half) as stochastic.h describes;
+// the row is global: the input may be rows row0 .. of a larger one.
 //
 // Work mapping: as quantize.hip, four consecutive lanes own one 32-element
 // block (16 bytes each) and every load instruction of a wave covers 1 KiB of
@@ -74,7 +75,7 @@ __device__ __forceinline__ void block_coords(int64_t blk, int64_t nb, double inv
 
 __global__ __launch_bounds__(kThreads) void quantize_sr_kernel(
     const u32x4_t* __restrict__ x, uint32_t* __restrict__ codes, uint8_t* __restrict__ scales,
-    int64_t nquarters, int64_t nb, double inv_nb, uint32_t key0, uint32_t key1) {
+    int64_t nquarters, int64_t nb, double inv_nb, uint32_t row0, uint32_t key0, uint32_t key1) {
   const int lane = threadIdx.x & 63;
   const int64_t wave = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
   const int64_t base = wave * (64 * kUnroll) + lane;
@@ -92,7 +93,7 @@ __global__ __launch_bounds__(kThreads) void quantize_sr_kernel(
     // This lane's draw: its half block in load 2g + odd.
     uint32_t row, col;
     block_coords((base + (int64_t)(2 * g + odd) * 64) >> 2, nb, inv_nb, row, col);
-    const Draw d = philox4x32_10(col, row, kDirRowwise, half, key0, key1);
+    const Draw d = philox4x32_10(col, row0 + row, kDirRowwise, half, key0, key1);
     // The even lane holds bytes 0..7 of its half in load 2g and needs bytes
     // 0..7 of load 2g + 1 (the odd lane's draw); the odd lane the reverse.
     const uint32_t got0 = swap_pair(odd ? d.w[0] : d.w[2]);
@@ -122,8 +123,8 @@ __global__ __launch_bounds__(kThreads) void quantize_sr_kernel(
 
 }  // namespace
 
-hipError_t launch_quantize_sr(const void* x_bf16, int64_t M, int64_t K, uint64_t seed,
-                              void* codes, void* scales, hipStream_t stream) {
+hipError_t launch_quantize_sr(const void* x_bf16, int64_t M, int64_t K, int64_t row0,
+                              uint64_t seed, void* codes, void* scales, hipStream_t stream) {
   const int64_t nb = K / 32;
   const int64_t nquarters = M * nb * 4;
   const int64_t per_block = (int64_t)kThreads * kUnroll;  // quarters per workgroup
@@ -131,7 +132,7 @@ hipError_t launch_quantize_sr(const void* x_bf16, int64_t M, int64_t K, uint64_t
   hipLaunchKernelGGL(quantize_sr_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream,
                      static_cast<const u32x4_t*>(x_bf16), static_cast<uint32_t*>(codes),
                      static_cast<uint8_t*>(scales), nquarters, nb, 1.0 / (double)nb,
-                     (uint32_t)seed, (uint32_t)(seed >> 32));
+                     (uint32_t)row0, (uint32_t)seed, (uint32_t)(seed >> 32));
   return hipGetLastError();
 }
 

@@ -110,6 +110,23 @@ int mxfp4_quantize_2d_sr(const void* x_bf16, int64_t M, int64_t K, uint64_t seed
                          void* codes_row, void* scales_row, void* codes_col,
                          void* scales_col, void* stream);
 
+/* Row shards of the two calls above, for a caller that splits a larger X
+ * over devices or calls: x_bf16 [M, K] holds rows row0 .. row0 + M - 1 of
+ * it, and the random bytes are keyed by those global rows (row-wise output
+ * row r of the shard draws as row row0 + r) and, column-wise, by the global
+ * row block row0 / 32 + j, so each output is exactly the matching part of
+ * the whole input's: rows row0 .. of the row-wise codes and scales, and
+ * (column-wise, written as [K, M/2] and [K, M/32] for the shard) columns
+ * row0 / 2 .. of its codes and row0 / 32 .. of its scales. row0 = 0 is
+ * the plain call. Requires 0 <= row0 and row0 + M <= 2^31 - 1, and for the
+ * bidimensional form row0 % 32 == 0; otherwise MXFP4_EINVAL. The rest as
+ * the plain calls. */
+int mxfp4_quantize_sr_rows(const void* x_bf16, int64_t M, int64_t K, int64_t row0,
+                           uint64_t seed, void* codes_out, void* scales_out, void* stream);
+int mxfp4_quantize_2d_sr_rows(const void* x_bf16, int64_t M, int64_t K, int64_t row0,
+                              uint64_t seed, void* codes_row, void* scales_row,
+                              void* codes_col, void* scales_col, void* stream);
+
 /* Block-scaled GEMM, TN: C[m, n] = sum_k dq(A[m, k]) * dq(B[n, k]) with
  * dq(code, scale) = E2M1(code) * 2^(scale - 127), fp32 accumulation; the
  * capability gates of the hipBLASLt MXFP4 path on "Integrate MXFP4 hipblaslt

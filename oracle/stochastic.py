@@ -33,6 +33,10 @@ Readings taken here (the pages leave them open):
       whenever |v| >= 1/4 (frac then has at most 8 bits); below that the
       result is biased toward zero by less than 1/256 of the grid spacing.
   S4  The sign bit of x is kept, also on magnitude 0 (as in R3 of mxfp4_ref).
+  S5  "The block's coordinates" are its coordinates in the whole input: a
+      part of X holding rows row0 .. row0 + M - 1 draws with the global rows
+      (rowwise) and the global row blocks row0 / 32 + j (columnwise), so that
+      its outputs are the matching part of the whole input's.
 Everything below is computed exactly (integers and float64).
 """
 
@@ -87,16 +91,17 @@ def seed_key(seed):
     return seed & 0xFFFFFFFF, seed >> 32
 
 
-def sr_random_bytes(row_ids, nblocks, seed, direction):
+def sr_random_bytes(row_ids, nblocks, seed, direction, block0=0):
     """S2: the random byte of every element of the given rows.
 
     row_ids: row indices r (of the output being written); nblocks: blocks
-    per row. Returns uint8 [len(row_ids), nblocks * 32].
+    per row, whose block columns are block0 .. block0 + nblocks - 1 (S5).
+    Returns uint8 [len(row_ids), nblocks * 32].
     """
     rows = np.asarray(row_ids, dtype=np.int64).reshape(-1)
     R = rows.size
     ctr = np.zeros((R, nblocks, 2, 4), dtype=np.uint32)
-    ctr[..., 0] = np.arange(nblocks, dtype=np.uint32)[None, :, None]
+    ctr[..., 0] = (block0 + np.arange(nblocks, dtype=np.int64)).astype(np.uint32)[None, :, None]
     ctr[..., 1] = rows.astype(np.uint32)[:, None, None]
     ctr[..., 2] = np.uint32(direction)
     ctr[..., 3] = np.arange(2, dtype=np.uint32)[None, None, :]
@@ -144,29 +149,35 @@ def quantize_sr_with_bytes(x_bits, rand_bytes):
     return codes.astype(np.uint8), scales
 
 
-def quantize_sr(x_bits, seed, direction=DIR_ROWWISE, row_ids=None):
-    """Row-wise MXFP4 with stochastic rounding (S1-S4).
+def quantize_sr(x_bits, seed, direction=DIR_ROWWISE, row_ids=None, block0=0):
+    """Row-wise MXFP4 with stochastic rounding (S1-S5).
 
     x_bits: uint16 [M, K] BF16 bits. row_ids: the output row index of each
-    given row (default 0..M-1), so that sampled rows of a large input take
-    the random bytes of their real coordinates.
+    given row (default 0..M-1), so that sampled rows, or a row shard, of a
+    large input take the random bytes of their real coordinates; block0: the
+    global block column of the first block of a row.
     """
     x_bits = np.asarray(x_bits, dtype=np.uint16)
     M, K = x_bits.shape
     if row_ids is None:
         row_ids = np.arange(M)
-    rb = sr_random_bytes(row_ids, K // BLOCK, seed, direction)
+    rb = sr_random_bytes(row_ids, K // BLOCK, seed, direction, block0)
     return quantize_sr_with_bytes(x_bits, rb)
 
 
-def quantize_2d_sr(x_bits, seed):
+def quantize_2d_sr(x_bits, seed, row0=0):
     """Rowwise (direction 0) and columnwise (direction 1: the rowwise form of
-    X^T) stochastic-rounding MXFP4 of X [M, K], M and K multiples of 32.
+    X^T) stochastic-rounding MXFP4 of X [M, K], M and K multiples of 32;
+    X may be rows row0 .. row0 + M - 1 of a larger input (row0 % 32 == 0, S5).
 
     Returns (codes [M, K/2], scales [M, K/32], codes_t [K, M/2], scales_t
     [K, M/32]).
     """
     x_bits = np.asarray(x_bits, dtype=np.uint16)
-    codes, scales = quantize_sr(x_bits, seed, DIR_ROWWISE)
-    codes_t, scales_t = quantize_sr(np.ascontiguousarray(x_bits.T), seed, DIR_COLUMNWISE)
+    if row0 % BLOCK:
+        raise ValueError("row0 must be a multiple of 32")
+    M = x_bits.shape[0]
+    codes, scales = quantize_sr(x_bits, seed, DIR_ROWWISE, row_ids=row0 + np.arange(M))
+    codes_t, scales_t = quantize_sr(np.ascontiguousarray(x_bits.T), seed, DIR_COLUMNWISE,
+                                    block0=row0 // BLOCK)
     return codes, scales, codes_t, scales_t

@@ -28,6 +28,8 @@ def main(path):
         "mxfp4_quantize_2d": ([vp, i64, i64, vp, vp, vp, vp, vp], i32),
         "mxfp4_quantize_sr": ([vp, i64, i64, u64, vp, vp, vp], i32),
         "mxfp4_quantize_2d_sr": ([vp, i64, i64, u64, vp, vp, vp, vp, vp], i32),
+        "mxfp4_quantize_sr_rows": ([vp, i64, i64, i64, u64, vp, vp, vp], i32),
+        "mxfp4_quantize_2d_sr_rows": ([vp, i64, i64, i64, u64, vp, vp, vp, vp, vp], i32),
         "mxfp4_gemm": ([vp, vp, vp, vp, i64, i64, i64, i32, vp, vp], i32),
         "mxfp4_gemm_tile": ([vp, vp, vp, vp, i64, i64, i64, i32, vp, vp], i32),
         "mxfp4_gemm_swiglu": ([vp, vp, vp, vp, i64, i64, i64, vp, vp, vp, vp], i32),
@@ -91,6 +93,11 @@ def main(path):
         expect(L.mxfp4_quantize_2d(P, M, K, P, P, P, P, None), EINVAL, f"2d {M}x{K}")
         expect(L.mxfp4_quantize_2d_sr(P, M, K, 3, P, P, P, P, None), EINVAL, "2d_sr")
     expect(L.mxfp4_quantize_2d(P, 32, 32, P, P, P + 8, P, None), EALIGN, "2d align")
+    for M, row0 in [(4, -1), (4, (1 << 31) - 4), ((1 << 31) - 1, 1)]:
+        expect(L.mxfp4_quantize_sr_rows(P, M, 32, row0, 7, P, P, None), EINVAL, "sr_rows")
+    for row0 in (-32, 16, (1 << 31) - 64):
+        expect(L.mxfp4_quantize_2d_sr_rows(P, 64, 64, row0, 3, P, P, P, P, None), EINVAL,
+               "2d_sr_rows")
     for M, N, K in [(32, 128, 256), (32, 256, 128), (0, 256, 256)]:
         expect(L.mxfp4_gemm_swiglu(P, P, P, P, M, N, K, P, P, None, None), EINVAL, "swiglu")
     expect(L.mxfp4_gemm_swiglu(P, P, P, P, 32, 256, 256, P, P, P + 8, None), EALIGN,
@@ -120,6 +127,9 @@ def main(path):
         expect(L.mxfp4_quantize_2d(P, 32, 32, P, P, P, P, None), U, "2d")
         expect(L.mxfp4_quantize_sr(P, 4, 32, 5, P, P, None), U, "sr")
         expect(L.mxfp4_quantize_2d_sr(P, 32, 32, 5, P, P, P, P, None), U, "2d_sr")
+        expect(L.mxfp4_quantize_sr_rows(P, 4, 32, 64, 5, P, P, None), U, "sr_rows")
+        expect(L.mxfp4_quantize_2d_sr_rows(P, 32, 32, 64, 5, P, P, P, P, None), U,
+               "2d_sr_rows")
         expect(L.mxfp4_gemm_swiglu(P, P, P, P, 32, 256, 256, P, P, None, None), U, "swiglu")
         expect(L.mxfp4_shuffle_b(P, P, 32, 256, P, P, None), U, "shuffle")
         expect(L.mxfp4_gemm_bshuffled(P, P, P, P, 32, 32, 256, 0, P, None), U, "bshuffled")

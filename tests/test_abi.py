@@ -33,8 +33,9 @@ def test_library_exports_every_declared_symbol():
     names = _declared_functions()
     assert names == ["mxfp4_available", "mxfp4_gemm", "mxfp4_gemm_bshuffled",
                      "mxfp4_gemm_frag", "mxfp4_gemm_swiglu", "mxfp4_gemm_tile", "mxfp4_quantize",
-                     "mxfp4_quantize_2d", "mxfp4_quantize_2d_sr", "mxfp4_quantize_async",
-                     "mxfp4_quantize_frag", "mxfp4_quantize_sr", "mxfp4_shuffle_b",
+                     "mxfp4_quantize_2d", "mxfp4_quantize_2d_sr", "mxfp4_quantize_2d_sr_rows",
+                     "mxfp4_quantize_async", "mxfp4_quantize_frag", "mxfp4_quantize_sr",
+                     "mxfp4_quantize_sr_rows", "mxfp4_shuffle_b",
                      "mxfp4_shuffle_b_sizes", "mxfp4_strerror", "mxfp4_to_frag"]
     for n in names:
         assert hasattr(lib, n), n
@@ -156,6 +157,20 @@ def test_quantize_rejects_bad_sizes(M, K):
     assert mx.mxfp4_quantize_sr(P16, M, K, 7, P16, P16, None) == EINVAL
 
 
+@pytest.mark.parametrize("M,row0", [(4, -1), (4, (1 << 31) - 4), (1, (1 << 31) - 1),
+                                    ((1 << 31) - 1, 1)])
+def test_quantize_sr_rows_rejects_bad_offsets(M, row0):
+    """A row shard must lie within rows 0 .. 2^31 - 2 of the whole input."""
+    assert mx.mxfp4_quantize_sr_rows(P16, M, 32, row0, 7, P16, P16, None) == EINVAL
+
+
+@pytest.mark.parametrize("row0", [-32, 16, 1, (1 << 31) - 64])
+def test_quantize_2d_sr_rows_rejects_bad_offsets(row0):
+    """Bidimensional shards start on a 32-row block and stay below 2^31 - 1 rows."""
+    assert mx.mxfp4_quantize_2d_sr_rows(P16, 64, 64, row0, 3, P16, P16, P16, P16,
+                                        None) == EINVAL
+
+
 def test_quantize_rejects_nulls_and_misalignment():
     assert mx.mxfp4_quantize(None, 4, 32, P16, P16) == EINVAL
     assert mx.mxfp4_quantize(P16, 4, 32, None, P16) == EINVAL
@@ -213,6 +228,9 @@ def test_no_device_reports_unsupported():
     assert mx.mxfp4_gemm_bshuffled(P16, P16, P16, P16, 32, 32, 256, mx.OUT_BF16, P16,
                                    None) == EUNSUPPORTED
     assert mx.mxfp4_quantize_2d_sr(P16, 32, 32, 5, P16, P16, P16, P16, None) == EUNSUPPORTED
+    assert mx.mxfp4_quantize_sr_rows(P16, 4, 32, 64, 5, P16, P16, None) == EUNSUPPORTED
+    assert mx.mxfp4_quantize_2d_sr_rows(P16, 32, 32, 64, 5, P16, P16, P16, P16,
+                                        None) == EUNSUPPORTED
     assert mx.mxfp4_quantize_frag(P16, 32, 256, P16, P16, None) == EUNSUPPORTED
     assert mx.mxfp4_to_frag(P16, P16, 32, 256, P16, P16, None) == EUNSUPPORTED
     assert mx.mxfp4_gemm_frag(P16, P16, P16, P16, 32, 32, 256, mx.OUT_BF16, P16,

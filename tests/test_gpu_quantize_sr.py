@@ -205,3 +205,29 @@ def test_sr_2d_workload(name):
                                   oracle.DIR_COLUMNWISE, row_ids=cols)
     _diff("codes_t", gct.cpu().numpy()[cols], rct)
     _diff("scales_t", gst.cpu().numpy()[cols], rst)
+
+
+@pytest.mark.parametrize("row0,m", [(0, 160), (160, 96), (256, 256), (480, 32)])
+def test_sr_row_shard_is_part_of_the_whole(row0, m):
+    """mxfp4_quantize_sr_rows and mxfp4_quantize_2d_sr_rows on rows row0 ..
+    row0 + m - 1 of X [512, 384]: byte for byte the matching part of the
+    whole input's outputs, and equal to the oracle keyed by global rows."""
+    announce(f"quantize_sr row shard {row0}+{m}")
+    bits = bf16_matrix((512, 384), ("laplace", 1.0), 23)
+    seed = 0x5EED
+    x = bf16_to_dev(bits)
+    wc, ws = [t.cpu().numpy() for t in mx.quantize_sr(x, seed)]
+    wc2, ws2, wct, wst = [t.cpu().numpy() for t in mx.quantize_2d_sr(x, seed)]
+    part = bf16_to_dev(np.ascontiguousarray(bits[row0:row0 + m]))
+    pc, ps = [t.cpu().numpy() for t in mx.quantize_sr(part, seed, row0=row0)]
+    qc, qs, qct, qst = [t.cpu().numpy() for t in mx.quantize_2d_sr(part, seed, row0=row0)]
+    torch.cuda.synchronize()
+    _diff("codes", pc, wc[row0:row0 + m])
+    _diff("scales", ps, ws[row0:row0 + m])
+    _diff("2d codes", qc, wc2[row0:row0 + m])
+    _diff("2d scales", qs, ws2[row0:row0 + m])
+    _diff("codes_t", qct, wct[:, row0 // 2:(row0 + m) // 2])
+    _diff("scales_t", qst, wst[:, row0 // 32:(row0 + m) // 32])
+    ref = oracle.quantize_2d_sr(np.ascontiguousarray(bits[row0:row0 + m]), seed, row0=row0)
+    for name, g, r in zip(("codes", "scales", "codes_t", "scales_t"), (qc, qs, qct, qst), ref):
+        _diff("oracle " + name, g, r)

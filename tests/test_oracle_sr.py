@@ -7,7 +7,9 @@ exhaustive enumeration of every random byte for every BF16 value, checked
 exactly (float64 on dyadic values, rationals on samples): each result is one
 of the two grid neighbours found by search, the bytes that round up are the
 largest ones, and the mean over all bytes is the input itself wherever frac
-has at most 8 bits. Readings S1-S4 are those stated in oracle/stochastic.py.
+has at most 8 bits; a row shard keyed by its global rows (reading S5) gives the
+matching part of the whole input's outputs. Readings S1-S5 are those stated in
+oracle/stochastic.py.
 """
 
 import os
@@ -282,3 +284,24 @@ def test_sr_seed_changes_codes_and_is_deterministic():
     assert np.array_equal(a, b)
     assert not np.array_equal(a, c)
     assert not np.array_equal(a, d)
+
+
+def test_sr_row_shards_are_parts_of_the_whole():
+    """Reading S5: a row shard keyed by its global rows and row blocks gives
+    exactly the matching rows (row-wise) and columns (column-wise) of the
+    whole input's outputs, and keying it from row 0 instead does not."""
+    x = bf16_matrix((160, 96), ("laplace", 1.0), 17)
+    c, s, ct, st = oracle.quantize_2d_sr(x, 99)
+    for row0, m in [(0, 64), (32, 96), (128, 32)]:
+        part = x[row0:row0 + m]
+        pc, ps, pct, pst = oracle.quantize_2d_sr(part, 99, row0=row0)
+        assert np.array_equal(pc, c[row0:row0 + m]) and np.array_equal(ps, s[row0:row0 + m])
+        assert np.array_equal(pct, ct[:, row0 // 2:(row0 + m) // 2])
+        assert np.array_equal(pst, st[:, row0 // 32:(row0 + m) // 32])
+        rc, rs = oracle.quantize_sr(part, 99, row_ids=row0 + np.arange(m))
+        assert np.array_equal(rc, pc) and np.array_equal(rs, ps)
+        if row0:
+            qc, _, qct, _ = oracle.quantize_2d_sr(part, 99)
+            assert not np.array_equal(qc, pc) and not np.array_equal(qct, pct)
+    with pytest.raises(ValueError):
+        oracle.quantize_2d_sr(x[16:48], 99, row0=16)
