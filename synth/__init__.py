@@ -127,3 +127,21 @@ def large_block_first(rows, K, big_scale):
     scales = np.full((rows, K // 32), big_scale - 8, np.uint8)
     scales[:, :8] = big_scale
     return codes, scales
+
+
+def device_random_bytes(shape, seed, lo=0, hi=255, device="cuda:0"):
+    """Uniform random bytes in [lo, hi], uint8 of `shape`, drawn on `device`
+    by torch's generator seeded with `seed`: for operands of gigabytes, too
+    large to draw on the host. The oracle reads the rows it checks back from
+    the device."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return torch.randint(lo, hi + 1, shape, generator=g, device=device, dtype=torch.uint8)
+
+
+def device_normal_bf16(shape, seed, device="cuda:0"):
+    """N(0, 1) BF16 values of `shape` drawn on `device` by torch's generator
+    seeded with `seed` (as device_random_bytes)."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return torch.randn(shape, generator=g, device=device, dtype=torch.bfloat16)
