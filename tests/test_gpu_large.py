@@ -1,12 +1,14 @@
 """GPU parity at sizes whose byte offsets pass 2^31 and 2^32.
 
-Operations: the row-wise and bidimensional quantize and the FP4 x FP4 GEMM
-("Initial integration of a4w4 GEMM", ROCm/TransformerEngine #663; gates of
-"Integrate MXFP4 hipblaslt GEMM support", #697, Changes list), whose
-contract admits every buffer under 2^40 bytes. Each kernel forms 64-bit row
-bases and 32-bit offsets within a tile; these cases put checked rows on both
-sides of the 2^31- and 2^32-byte marks of the quantize input, of A's and B's
-codes and of C, on the tile, split-K, pre-shuffled and fragment-order paths.
+Operations: the row-wise and bidimensional quantize, round to nearest and
+stochastic, and the FP4 x FP4 GEMM ("Initial integration of a4w4 GEMM",
+ROCm/TransformerEngine #663; gates of "Integrate MXFP4 hipblaslt GEMM
+support", #697, Changes list) with its fused SwiGLU epilogue, whose contract
+admits every buffer under 2^40 bytes. Each kernel forms 64-bit row bases and
+32-bit offsets within a tile; these cases put checked rows on both sides of
+the 2^31- and 2^32-byte marks of the quantize input, of A's and B's codes, of
+C and of the BF16 activation, on the tile, split-K, pre-shuffled,
+fragment-order and fused SwiGLU paths.
 
 Operands of gigabytes are drawn on the GPU by torch's seeded generator
 (synth.device_random_bytes, synth.device_normal_bf16); the rows and columns
@@ -135,4 +137,60 @@ def test_gemm_b_past_2gib(M, out_dtype):
         assert torch.equal(got, out), "pre-shuffled GEMM differs from mxfp4_gemm"
         del bsh, bssh, got
     del ac, as_, bc, bs, out
+    _free()
+
+
+def test_quantize_sr_input_past_4gib():
+    """Stochastic rounding on the same 4 GiB shape: row-wise and both outputs
+    of the bidimensional form against the oracle's draws at the sampled
+    rows' own coordinates (rows past 2^31 and 2^32 bytes of X) and on whole
+    sampled columns."""
+    M, seed = (1 << 21) + 96, 0x0123456789ABCDEF
+    announce(f"stochastic quantize past 4 GiB: X [{M}, {K}]")
+    x = device_normal_bf16((M, K), 5031)
+    codes, scales = mx.quantize_sr(x, seed)
+    cr, sr, cc, sc = mx.quantize_2d_sr(x, seed)
+    torch.cuda.synchronize()
+    rows = _sample(M, 5032)
+    xb = bf16_bits_of_tensor(x[torch.from_numpy(rows).to(DEV)])
+    want_c, want_s = oracle.quantize_sr(xb, seed, oracle.DIR_ROWWISE, row_ids=rows)
+    for got_c, got_s in ((codes, scales), (cr, sr)):
+        assert np.array_equal(_rows(got_c, rows), want_c)
+        assert np.array_equal(_rows(got_s, rows), want_s)
+    cols = np.array([0, 1, 517, K - 1], dtype=np.int64)
+    xt = bf16_bits_of_tensor(x[:, torch.from_numpy(cols).to(DEV)].t().contiguous())
+    want_c, want_s = oracle.quantize_sr(xt, seed, oracle.DIR_COLUMNWISE, row_ids=cols)
+    assert np.array_equal(_rows(cc, cols), want_c)
+    assert np.array_equal(_rows(sc, cols), want_s)
+    print(f"[gpu] stochastic quantize past 4 GiB: {rows.size} rows, {cols.size} columns "
+          f"bit-exact", flush=True)
+    del x, codes, scales, cr, sr, cc, sc
+    _free()
+
+
+def test_gemm_swiglu_a_and_act_past_2gib():
+    """Fused SwiGLU gate+up GEMM with A [5 Mi, 1024] (2.5 GiB of codes) and
+    B = [W_gate; W_up] of 2 x 256 rows: the BF16 activation (2.5 GiB) within
+    the oracle's tolerance and its codes and scales bit-exact with the
+    oracle's quantize of it, at sampled rows past row 2^22."""
+    N = 512
+    announce(f"gemm_swiglu A past 2 GiB: {BIG}x{N}x{K}")
+    ac = device_random_bytes((BIG, K // 2), 5041)
+    as_ = device_random_bytes((BIG, K // 32), 5042, lo=122, hi=130)
+    bc = device_random_bytes((N, K // 2), 5043)
+    bs = device_random_bytes((N, K // 32), 5044, lo=112, hi=120)
+    codes, scales, act = mx.gemm_swiglu(ac, as_, bc, bs, want_act=True)
+    torch.cuda.synchronize()
+    rows = _sample(BIG, 5045)
+    rows_t = torch.from_numpy(rows).to(DEV)
+    ref, tol = oracle.swiglu_reference(_rows(ac, rows), _rows(as_, rows), bc.cpu().numpy(),
+                                       bs.cpu().numpy())
+    act_bits = bf16_bits_of_tensor(act[rows_t])
+    ok = oracle.check_act_bf16(act_bits, ref, tol)
+    assert ok.all(), f"{int((~ok).sum())} activations outside tolerance"
+    q_codes, q_scales = oracle.quantize(act_bits)
+    assert np.array_equal(_rows(codes, rows), q_codes)
+    assert np.array_equal(_rows(scales, rows), q_scales)
+    print(f"[gpu] gemm_swiglu A past 2 GiB: {rows.size} rows x {N // 2} activations", flush=True)
+    del ac, as_, bc, bs, codes, scales, act
     _free()
