@@ -89,6 +89,9 @@ def parse():
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="only run a plain device copy of this many MiB three times and exit "
                         "(the known-size kernel that scales the FETCH_SIZE/WRITE_SIZE counters)")
+    p.add_argument("--copy-rate-mib", type=int, default=0,
+                   help="only time a plain device copy of this many MiB (read + write rate, "
+                        "the practical ceiling of streaming kernels) and exit")
     return p.parse_args()
 
 
@@ -127,6 +130,36 @@ def copy_calibration(mib):
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}), flush=True)
+
+
+def copy_rate(mib):
+    """Read + write rate of a plain device-to-device copy of `mib` MiB: the
+    practical ceiling of kernels that stream HBM in and out. Two buffer pairs
+    (beyond the last-level cache) alternate; after 20 untimed copies, the
+    median of 10 groups of 10 copies, each group between one event pair on
+    the stream the copies run on."""
+    import torch
+    dev = torch.device("cuda:0")
+    n = mib << 20
+    pairs = [(torch.ones(n // 4, dtype=torch.float32, device=dev),
+              torch.empty(n // 4, dtype=torch.float32, device=dev)) for _ in range(2)]
+    for i in range(20):
+        src, dst = pairs[i % 2]
+        dst.copy_(src)
+    times = []
+    for _ in range(10):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(10):
+            src, dst = pairs[i % 2]
+            dst.copy_(src)
+        e1.record()
+        e1.synchronize()
+        times.append(e0.elapsed_time(e1) / 10)
+    us = sorted(times)[len(times) // 2] * 1e3
+    print(json.dumps({"copy_mib": mib, "copy_us": round(us, 2),
+                      "read_write_tb_per_s": round(2 * n / (us * 1e-6) / 1e12, 3),
+                      "frac_of_8_tb_per_s": round(2 * n / (us * 1e-6) / 8e12, 3)}), flush=True)
 
 
 def run_sections():
@@ -423,6 +456,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration_mib:
         copy_calibration(args.copy_calibration_mib)
+        return
+    if args.copy_rate_mib:
+        copy_rate(args.copy_rate_mib)
         return
     if args.probe:
         run_probe()
